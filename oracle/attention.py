@@ -1,0 +1,170 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. The product path (the HIP library and
+its Python binding) never calls it, and this module imports nothing from the
+product package.
+
+What it computes is the plain definition, with the score matrix materialised:
+"Why Fast GPUs Still Wait for Memory", section "Attention from first
+principles": S = Q K^T, P = softmax(S) row by row, O = P V. The same page,
+section "FlashAttention is an IO algorithm", states that the tiled online-softmax
+schedule changes only the memory traffic, not the arithmetic result, so the
+naive schedule written here is the exact reference for the fused kernels.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes):
+  * the score carries a caller-given factor: S = scale * Q K^T (the pages write
+    S = Q K^T; the configured workloads use scale = 1/sqrt(d));
+  * causal keeps the lower triangle including the diagonal (key j <= query i),
+    following the page's "Nuance - causal masking" note, with N_q = N_k;
+  * grouped-query attention maps query head h to KV head h // (H / H_kv)
+    (section "Attention III - KV cache, GQA, MLA" gives only g = h / h_kv);
+  * LSE is the natural-log log-sum-exp of each score row over unmasked keys;
+  * decode is one query row against the first kv_len[b] cache rows;
+  * the backward pass is the gradient of L = sum(O * dO) with respect to Q, K
+    and V, recomputing P from an explicit S (same page: "the backward pass does
+    more arithmetic, because S is recomputed rather than stored"; the MoA paper,
+    section 4.1, computes GQ, GK, GV the same way from Q, K, V).
+
+All arithmetic is in float64 numpy. Matrix products use numpy's matmul as the
+library primitive for a contraction; there is no tiling or reordering beyond
+the definition. Every function returns new arrays and keeps no state.
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _check_shapes(q, k, v):
+    B, H, N, d = q.shape
+    Bk, H_kv, Nk, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if H % H_kv != 0:
+        raise ValueError("H must be a multiple of H_kv")
+    return B, H, H_kv, N, d
+
+
+def _scores(qh: np.ndarray, kh: np.ndarray, causal: bool, scale: float) -> np.ndarray:
+    """Explicit score matrix S = scale * q k^T, masked entries set to -inf."""
+    s = scale * (qh @ kh.T)
+    if causal:
+        n_q, n_k = s.shape
+        above = np.triu(np.ones((n_q, n_k), dtype=bool), k=1)  # key j > query i
+        s[above] = -np.inf
+    return s
+
+
+def _softmax_rows(s: np.ndarray):
+    """Row softmax with the row maximum subtracted first; also returns ln-sum-exp."""
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    p = e / l
+    lse = (m + np.log(l))[:, 0]
+    return p, lse
+
+
+def attention_fwd(q, k, v, causal: bool, scale: float):
+    """O [B,H,N,d] and LSE [B,H,N] for q [B,H,N,d], k/v [B,H_kv,N,d] (float64)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, H_kv, N, d = _check_shapes(q, k, v)
+    g = H // H_kv
+    o = np.empty((B, H, N, d))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            hk = h // g
+            s = _scores(q[b, h], k[b, hk], causal, scale)
+            p, lse[b, h] = _softmax_rows(s)
+            o[b, h] = p @ v[b, hk]
+    return o, lse
+
+
+def attention_fwd_rows(q, k, v, causal: bool, scale: float, rows):
+    """O and LSE for selected (b, h, i) query rows only, each from its own score row.
+
+    rows: integer array [n, 3] of (b, h, i). Returns (o [n, d], lse [n]).
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, H_kv, N, d = _check_shapes(q, k, v)
+    g = H // H_kv
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    o = np.empty((len(rows), d))
+    lse = np.empty(len(rows))
+    for r, (b, h, i) in enumerate(rows):
+        hk = h // g
+        n_keys = i + 1 if causal else N  # causal row i sees keys 0..i
+        s = scale * (k[b, hk, :n_keys] @ q[b, h, i])
+        p, lse_r = _softmax_rows(s[None, :])
+        o[r] = p[0] @ v[b, hk, :n_keys]
+        lse[r] = lse_r[0]
+    return o, lse
+
+
+def attention_decode(q, k_cache, v_cache, kv_len, scale: float):
+    """One query per (sequence, head) over its first kv_len[b] cached keys.
+
+    q [B,H,d]; k_cache/v_cache [B,H_kv,N_cap,d]; kv_len [B] ints in [1, N_cap].
+    Returns (o [B,H,d], lse [B,H]). Cache rows at or beyond kv_len[b] are not read.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, d = q.shape
+    H_kv = k_cache.shape[1]
+    g = H // H_kv
+    o = np.empty((B, H, d))
+    lse = np.empty((B, H))
+    for b in range(B):
+        n = int(kv_len[b])
+        if not 1 <= n <= k_cache.shape[2]:
+            raise ValueError("kv_len out of range")
+        for h in range(H):
+            hk = h // g
+            kh = np.asarray(k_cache[b, hk, :n], dtype=np.float64)
+            vh = np.asarray(v_cache[b, hk, :n], dtype=np.float64)
+            s = scale * (kh @ q[b, h])
+            p, lse_r = _softmax_rows(s[None, :])
+            o[b, h] = p[0] @ vh
+            lse[b, h] = lse_r[0]
+    return o, lse
+
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float):
+    """Gradients of L = sum(O * dO) for O = softmax(scale Q K^T [mask]) V.
+
+    Returns (dq [B,H,N,d], dk [B,H_kv,N,d], dv [B,H_kv,N,d], o, lse). Under grouped
+    heads, dK and dV of a KV head sum the contributions of its query heads.
+    Steps, per (b, h), with P recomputed from the explicit S:
+        dV += P^T dO
+        dP  = dO V^T
+        D_i = sum_t dO[i,t] O[i,t]          (= sum_j P_ij dP_ij)
+        dS  = P * (dP - D)                   (zero where masked, since P is zero)
+        dQ  = scale * dS K
+        dK += scale * dS^T Q
+    """
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, H, H_kv, N, d = _check_shapes(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    g = H // H_kv
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            hk = h // g
+            s = _scores(q[b, h], k[b, hk], causal, scale)
+            p, lse[b, h] = _softmax_rows(s)
+            o[b, h] = p @ v[b, hk]
+            dv[b, hk] += p.T @ dout[b, h]
+            dp = dout[b, h] @ v[b, hk].T
+            D = np.sum(dout[b, h] * o[b, h], axis=1, keepdims=True)
+            ds = p * (dp - D)
+            dq[b, h] = scale * (ds @ k[b, hk])
+            dk[b, hk] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv, o, lse

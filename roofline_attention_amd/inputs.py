@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs for the attention path and its oracle.
+
+This module is shared by the HIP path's tests/benchmark and by the oracle's
+checks. It holds no attention arithmetic: it only draws random numbers, rounds
+them to the storage dtype and lays them out.
+
+Recipe (the pages fix none of it; the workloads are synthetic sweeps shaped like
+"Why Fast GPUs Still Wait for Memory", section "Attention from first principles"
+(N = 4096, d = 128, bf16) and the MoA paper's section 2.2 (B = 2, D = 64)):
+
+* every (tensor, batch, head) block is drawn from its own numpy stream,
+  ``Generator(PCG64(SeedSequence([seed, tensor_id, b, h])))``, as
+  ``standard_normal(shape, dtype=float32)``; a per-block stream lets a checker
+  regenerate one head of a large tensor without drawing the rest;
+* tensor ids: q = 0, k = 1, v = 2, dO = 3, kv_len = 4;
+* an optional exact factor (0.5 for the large prefill workload) multiplies the
+  float32 sample before rounding;
+* bf16 storage uses round-to-nearest-even (torch's float32 -> bfloat16 cast);
+* decode KV lengths are integers drawn inclusively from [lo, hi]; cache rows at
+  or beyond a sequence's length are filled with NaN so that any read of them
+  shows up in the result.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO, TENSOR_KVLEN = 0, 1, 2, 3, 4
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One frozen case: operation, shape, dtype, mask and seed."""
+
+    name: str
+    op: str  # "fwd", "decode" or "fwdbwd"
+    B: int
+    H: int
+    H_kv: int
+    N: int  # sequence length (prefill) or cache capacity (decode)
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+    seed: int
+    qk_factor: float = 1.0  # exact factor applied to Q and K samples
+    kv_lo: int = 0  # decode only: inclusive KV-length range
+    kv_hi: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of the headline metric, in order.
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", "fwd", 1, 2, 2, 128, 64, "f32", False, seed=1),
+    "prefill_causal_1k": Workload("prefill_causal_1k", "fwd", 4, 16, 16, 1024, 64, "bf16", True, seed=2),
+    "prefill_4k_causal": Workload("prefill_4k_causal", "fwd", 2, 32, 32, 4096, 128, "bf16", True, seed=3,
+                                  qk_factor=0.5),
+    "prefill_4k": Workload("prefill_4k", "fwd", 2, 32, 32, 4096, 128, "bf16", False, seed=3, qk_factor=0.5),
+    "decode_gqa": Workload("decode_gqa", "decode", 64, 32, 8, 8192, 128, "bf16", False, seed=4,
+                           kv_lo=512, kv_hi=8192),
+    "fwdbwd_4k_causal": Workload("fwdbwd_4k_causal", "fwdbwd", 2, 16, 16, 4096, 128, "bf16", True, seed=5),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def normal_block(seed: int, tensor_id: int, b: int, h: int, shape, factor: float = 1.0) -> np.ndarray:
+    """float32 N(0,1) sample for one (tensor, batch, head) block."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor_id, b, h])))
+    x = g.standard_normal(shape, dtype=np.float32)
+    if factor != 1.0:
+        x *= np.float32(factor)  # 0.5 is exact in float32
+    return x
+
+
+def make_tensor(seed: int, tensor_id: int, B: int, H: int, rows: int, d: int, dtype: str,
+                factor: float = 1.0) -> torch.Tensor:
+    """[B, H, rows, d] CPU tensor in the storage dtype, one stream per (b, h)."""
+    out = torch.empty((B, H, rows, d), dtype=torch_dtype(dtype))
+    for b in range(B):
+        for h in range(H):
+            blk = torch.from_numpy(normal_block(seed, tensor_id, b, h, (rows, d), factor))
+            out[b, h].copy_(blk)  # float32 -> bf16 cast rounds to nearest even
+    return out
+
+
+def kv_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TENSOR_KVLEN])))
+    return g.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
+def make_prefill(w: Workload, with_dout: Optional[bool] = None) -> dict:
+    """q, k, v (and dO for fwd+bwd) as CPU tensors in the storage dtype."""
+    if with_dout is None:
+        with_dout = w.op == "fwdbwd"
+    t = {
+        "q": make_tensor(w.seed, TENSOR_Q, w.B, w.H, w.N, w.d, w.dtype, w.qk_factor),
+        "k": make_tensor(w.seed, TENSOR_K, w.B, w.H_kv, w.N, w.d, w.dtype, w.qk_factor),
+        "v": make_tensor(w.seed, TENSOR_V, w.B, w.H_kv, w.N, w.d, w.dtype),
+    }
+    if with_dout:
+        t["do"] = make_tensor(w.seed, TENSOR_DO, w.B, w.H, w.N, w.d, w.dtype)
+    return t
+
+
+def make_decode(w: Workload, nan_pad: bool = True) -> dict:
+    """q [B, H, d]; k/v caches [B, H_kv, N_cap, d]; kv_len [B] int32."""
+    kv_len = kv_lengths(w.seed, w.B, w.kv_lo, w.kv_hi)
+    q = make_tensor(w.seed, TENSOR_Q, w.B, w.H, 1, w.d, w.dtype, w.qk_factor)[:, :, 0, :].contiguous()
+    k = make_tensor(w.seed, TENSOR_K, w.B, w.H_kv, w.N, w.d, w.dtype, w.qk_factor)
+    v = make_tensor(w.seed, TENSOR_V, w.B, w.H_kv, w.N, w.d, w.dtype)
+    if nan_pad:
+        for b in range(w.B):
+            k[b, :, int(kv_len[b]):, :] = float("nan")
+            v[b, :, int(kv_len[b]):, :] = float("nan")
+    return {"q": q, "k": k, "v": v, "kv_len": torch.from_numpy(kv_len)}
+
+
+def decode_head_slices(w: Workload, b: int, hk: int, length: int):
+    """Regenerate the first `length` rows of one KV head of a decode cache (no NaN pad)."""
+    rows = w.N
+    k = torch.from_numpy(normal_block(w.seed, TENSOR_K, b, hk, (rows, w.d), w.qk_factor)[:length])
+    v = torch.from_numpy(normal_block(w.seed, TENSOR_V, b, hk, (rows, w.d))[:length])
+    return k.to(torch_dtype(w.dtype)), v.to(torch_dtype(w.dtype))
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact upcast of stored values for the fp64 oracle."""
+    return t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,90 @@
+"""Planted mistakes in the oracle, on the CPU: each must fail at least one pin.
+
+Each mutant is the oracle's own source with one plausible slip edited in (a
+dropped term, a wrong sign or index, a transposed operand, an off-by-one mask).
+The mutated copy is loaded as a separate module and the pin suite of
+test_oracle_pins is run against it; a mutant that passes every pin would mean the
+pins cannot tell that slip from the correct oracle.
+"""
+import importlib.util
+import inspect
+import os
+import types
+
+import pytest
+
+import oracle.attention as real_oracle
+from tests import test_oracle_pins as pins
+
+SRC = inspect.getsource(real_oracle)
+
+MUTANTS = {
+    "mask_drops_diagonal": ("np.triu(np.ones((n_q, n_k), dtype=bool), k=1)", "np.triu(np.ones((n_q, n_k), dtype=bool), k=0)"),
+    "mask_ignored": ("    if causal:\n        n_q, n_k = s.shape", "    if False:\n        n_q, n_k = s.shape"),
+    "scale_dropped": ("s = scale * (qh @ kh.T)", "s = (qh @ kh.T)"),
+    "operand_transposed": ("s = scale * (qh @ kh.T)", "s = scale * (kh @ qh.T)"),
+    "softmax_wrong_axis": ("l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)"),
+    "lse_missing_max": ("lse = (m + np.log(l))[:, 0]", "lse = (np.log(l))[:, 0]"),
+    "gqa_modulo_map": ("            hk = h // g\n            s = _scores", "            hk = h % H_kv\n            s = _scores"),
+    "bwd_drops_D": ("ds = p * (dp - D)", "ds = p * dp"),
+    "bwd_sign": ("ds = p * (dp - D)", "ds = p * (D - dp)"),
+    "bwd_dk_no_scale": ("dk[b, hk] += scale * (ds.T @ q[b, h])", "dk[b, hk] += (ds.T @ q[b, h])"),
+    "bwd_dv_transposed": ("dv[b, hk] += p.T @ dout[b, h]", "dv[b, hk] += p @ dout[b, h]"),
+    "rows_causal_off_by_one": ("n_keys = i + 1 if causal else N", "n_keys = i if causal else N"),
+    "decode_reads_one_short": ("kh = np.asarray(k_cache[b, hk, :n], dtype=np.float64)",
+                               "kh = np.asarray(k_cache[b, hk, :n - 1], dtype=np.float64)"),
+}
+
+# The pin suite, with the parameters each pin runs at.
+PIN_CALLS = [
+    (pins.test_fwd_matches_torch_sdpa, dict(B=2, H=4, H_kv=2, N=37, d=16, causal=False)),
+    (pins.test_fwd_matches_torch_sdpa, dict(B=2, H=4, H_kv=2, N=37, d=16, causal=True)),
+    (pins.test_fwd_scale_zero_is_uniform_average, dict(causal=True)),
+    (pins.test_fwd_single_key, {}),
+    (pins.test_fwd_rows_sum_to_one, {}),
+    (pins.test_fwd_constant_v, dict(causal=True)),
+    (pins.test_fwd_causal_row0, {}),
+    (pins.test_fwd_one_hot_selection_and_exact_lse, {}),
+    (pins.test_fwd_key_shift_moves_lse_only, dict(causal=True)),
+    (pins.test_fwd_gqa_equals_expanded_heads, {}),
+    (pins.test_fwd_rows_agree_with_full, dict(causal=True)),
+    (pins.test_decode_matches_sdpa_single_query_and_ignores_pad, {}),
+    (pins.test_decode_is_last_causal_row, {}),
+    (pins.test_bwd_matches_torch_autograd, dict(B=2, H=4, H_kv=2, N=23, d=8, causal=True)),
+    (pins.test_bwd_sum_invariants, dict(causal=True)),
+    (pins.test_bwd_constant_v_and_zero_scale, {}),
+    (pins.test_bwd_causal_last_key, {}),
+]
+
+
+def load_mutant(name: str) -> types.ModuleType:
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(SRC.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def pins_fail(mod) -> list:
+    failed = []
+    saved = pins.orc
+    pins.orc = mod
+    try:
+        for fn, kw in PIN_CALLS:
+            try:
+                fn(**kw)
+            except Exception as e:  # an assertion, or a crash the slip causes
+                failed.append((fn.__name__, type(e).__name__))
+    finally:
+        pins.orc = saved
+    return failed
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert pins_fail(real_oracle) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    failed = pins_fail(load_mutant(name))
+    assert failed, f"mutant {name} passed every pin"

@@ -1,0 +1,285 @@
+"""Pins for the fp64 oracle, each tied to something other than the oracle itself.
+
+Kinds of pin used (none re-types the oracle's formula):
+  * library routine: torch's scaled_dot_product_attention and autograd in float64
+    on the CPU, an implementation that shares no code with the oracle;
+  * closed forms: scale = 0 (uniform weights), N = 1, a one-hot construction
+    whose log-sum-exp has an exact value;
+  * invariants the pages fix ("Why Fast GPUs Still Wait for Memory", section
+    "Attention from first principles"): softmax rows sum to one, a constant V
+    gives a constant output, causal row 0 equals V[0], a large-scaled one-hot
+    Q.K selects one V row; plus permutation and shift invariance;
+  * brute force: central finite differences of L = sum(O * dO) on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as orc
+
+RNG = np.random.default_rng(12345)
+
+
+def rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+def sdpa(q, k, v, causal, scale):
+    """torch float64 CPU reference, with KV heads expanded for grouped queries."""
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    g = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(g, dim=1)
+    vt = vt.repeat_interleave(g, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale).numpy()
+
+
+# ---------------------------------------------------------------- forward ---
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 128, 64), (2, 4, 2, 37, 16), (1, 8, 1, 65, 32), (2, 3, 3, 1, 8)])
+def test_fwd_matches_torch_sdpa(B, H, H_kv, N, d, causal):
+    q, k, v = rand(B, H, N, d), rand(B, H_kv, N, d), rand(B, H_kv, N, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = orc.attention_fwd(q, k, v, causal, scale)
+    np.testing.assert_allclose(o, sdpa(q, k, v, causal, scale), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_scale_zero_is_uniform_average(causal):
+    B, H, N, d = 1, 2, 50, 8
+    q, k, v = rand(B, H, N, d), rand(B, H, N, d), rand(B, H, N, d)
+    o, lse = orc.attention_fwd(q, k, v, causal, 0.0)
+    if causal:
+        counts = np.arange(1, N + 1)
+        want = np.cumsum(v, axis=2) / counts[None, None, :, None]
+        want_lse = np.broadcast_to(np.log(counts), lse.shape)
+    else:
+        want = np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape)
+        want_lse = np.full(lse.shape, math.log(N))
+    np.testing.assert_allclose(o, want, atol=1e-13)
+    np.testing.assert_allclose(lse, want_lse, atol=1e-13)
+
+
+def test_fwd_single_key():
+    q, k, v = rand(1, 3, 1, 16), rand(1, 3, 1, 16), rand(1, 3, 1, 16)
+    scale = 0.37
+    o, lse = orc.attention_fwd(q, k, v, False, scale)
+    np.testing.assert_array_equal(o, v)
+    np.testing.assert_allclose(lse[..., 0], scale * np.sum(q[:, :, 0] * k[:, :, 0], axis=-1), atol=1e-14)
+
+
+def test_fwd_rows_sum_to_one():
+    # With V the identity (d = N), O = P itself.
+    N = 48
+    q, k = rand(1, 2, N, N), rand(1, 2, N, N)
+    v = np.broadcast_to(np.eye(N), (1, 2, N, N)).copy()
+    for causal in (False, True):
+        p, _ = orc.attention_fwd(q, k, v, causal, 0.2)
+        assert (p >= 0).all()
+        np.testing.assert_allclose(p.sum(axis=-1), 1.0, atol=1e-13)
+        if causal:
+            assert np.all(np.triu(p[0, 0], k=1) == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_constant_v(causal):
+    N, d = 64, 16
+    q, k = rand(1, 2, N, d), rand(1, 2, N, d)
+    c = rand(d)
+    v = np.broadcast_to(c, (1, 2, N, d)).copy()
+    o, _ = orc.attention_fwd(q, k, v, causal, 0.25)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-13)
+
+
+def test_fwd_causal_row0():
+    q, k, v = rand(2, 2, 40, 16), rand(2, 2, 40, 16), rand(2, 2, 40, 16)
+    scale = 0.3
+    o, lse = orc.attention_fwd(q, k, v, True, scale)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], scale * np.sum(q[:, :, 0] * k[:, :, 0], -1), atol=1e-14)
+
+
+def one_hot_case(N, d, c, scale, perm_seed=0):
+    """k_j = e_j (j < d), 0 otherwise; q_i = c e_sigma(i); so S_ij = scale*c*[j == sigma(i)]."""
+    k = np.zeros((1, 1, N, d))
+    k[0, 0, np.arange(d), np.arange(d)] = 1.0
+    sigma = np.random.default_rng(perm_seed).integers(0, d, size=N)
+    q = np.zeros((1, 1, N, d))
+    q[0, 0, np.arange(N), sigma] = c
+    v = rand(1, 1, N, d)
+    return q, k, v, sigma
+
+
+def test_fwd_one_hot_selection_and_exact_lse():
+    N, d, c, scale = 128, 64, 600.0, 0.125  # scale * c = 75
+    q, k, v, sigma = one_hot_case(N, d, c, scale)
+    o, lse = orc.attention_fwd(q, k, v, False, scale)
+    np.testing.assert_allclose(o[0, 0], v[0, 0, sigma], atol=N * math.exp(-75) * 10)
+    # lse_i = ln(e^{scale c} + (N - 1) e^0), a closed form
+    np.testing.assert_allclose(lse[0, 0], scale * c + math.log1p((N - 1) * math.exp(-scale * c)), rtol=1e-15)
+    # a small logit gap: exact weights e^{a}/(e^{a}+N-1) on the selected row, 1/(e^a+N-1) elsewhere
+    a = 1.5
+    o2, lse2 = orc.attention_fwd(q * (a / (scale * c)), k, v, False, scale)
+    z = math.exp(a) + N - 1
+    want = (v[0, 0].sum(axis=0)[None, :] + (math.exp(a) - 1.0) * v[0, 0, sigma]) / z
+    np.testing.assert_allclose(o2[0, 0], want, atol=1e-13)
+    np.testing.assert_allclose(lse2[0, 0], math.log(z), atol=1e-14)
+
+
+def test_fwd_permutation_invariance():
+    N, d = 33, 8
+    q, k, v = rand(1, 1, N, d), rand(1, 1, N, d), rand(1, 1, N, d)
+    o, lse = orc.attention_fwd(q, k, v, False, 0.4)
+    pk = RNG.permutation(N)
+    pq = RNG.permutation(N)
+    o2, lse2 = orc.attention_fwd(q[:, :, pq], k[:, :, pk], v[:, :, pk], False, 0.4)
+    np.testing.assert_allclose(o2, o[:, :, pq], atol=1e-13)
+    np.testing.assert_allclose(lse2, lse[:, :, pq], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_key_shift_moves_lse_only(causal):
+    # Adding u to every key adds scale*q_i.u to the whole score row i.
+    N, d, scale = 40, 8, 0.3
+    q, k, v = rand(1, 2, N, d), rand(1, 2, N, d), rand(1, 2, N, d)
+    u = rand(d)
+    o, lse = orc.attention_fwd(q, k, v, causal, scale)
+    o2, lse2 = orc.attention_fwd(q, k + u, v, causal, scale)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + scale * (q @ u), atol=1e-12)
+
+
+def test_fwd_gqa_equals_expanded_heads():
+    B, H, H_kv, N, d = 1, 8, 2, 20, 8
+    q, k, v = rand(B, H, N, d), rand(B, H_kv, N, d), rand(B, H_kv, N, d)
+    o, lse = orc.attention_fwd(q, k, v, True, 0.3)
+    # query heads 0..3 read KV head 0, heads 4..7 read KV head 1
+    o_a, lse_a = orc.attention_fwd(q[:, :4], k[:, :1], v[:, :1], True, 0.3)
+    np.testing.assert_array_equal(o[:, :4], o_a)
+    o_b, _ = orc.attention_fwd(q[:, 4:], k[:, 1:], v[:, 1:], True, 0.3)
+    np.testing.assert_array_equal(o[:, 4:], o_b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_rows_agree_with_full(causal):
+    B, H, H_kv, N, d = 2, 4, 2, 70, 16
+    q, k, v = rand(B, H, N, d), rand(B, H_kv, N, d), rand(B, H_kv, N, d)
+    o, lse = orc.attention_fwd(q, k, v, causal, 0.25)
+    rows = np.array([[0, 0, 0], [1, 3, 69], [0, 2, 35], [1, 1, 1]])
+    o_r, lse_r = orc.attention_fwd_rows(q, k, v, causal, 0.25, rows)
+    np.testing.assert_allclose(o_r, o[rows[:, 0], rows[:, 1], rows[:, 2]], atol=1e-13)
+    np.testing.assert_allclose(lse_r, lse[rows[:, 0], rows[:, 1], rows[:, 2]], atol=1e-13)
+    np.testing.assert_allclose(o_r, sdpa(q, k, v, causal, 0.25)[rows[:, 0], rows[:, 1], rows[:, 2]], atol=1e-12)
+
+
+# ----------------------------------------------------------------- decode ---
+
+def test_decode_matches_sdpa_single_query_and_ignores_pad():
+    B, H, H_kv, N_cap, d = 3, 8, 2, 50, 16
+    q = rand(B, H, d)
+    kc, vc = rand(B, H_kv, N_cap, d), rand(B, H_kv, N_cap, d)
+    kv_len = np.array([1, 17, 50])
+    for b in range(B):
+        kc[b, :, kv_len[b]:] = np.nan
+        vc[b, :, kv_len[b]:] = np.nan
+    scale = 0.25
+    o, lse = orc.attention_decode(q, kc, vc, kv_len, scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    for b in range(B):
+        n = kv_len[b]
+        want = sdpa(q[b][None, :, None, :], kc[b][None, :, :n], vc[b][None, :, :n], False, scale)
+        np.testing.assert_allclose(o[b], want[0, :, 0], atol=1e-12)
+    # length 1 gives that row's V exactly
+    np.testing.assert_array_equal(o[0], np.repeat(vc[0, :, 0], H // H_kv, axis=0))
+
+
+def test_decode_is_last_causal_row():
+    B, H, H_kv, N, d = 1, 4, 1, 30, 8
+    q, k, v = rand(B, H, N, d), rand(B, H_kv, N, d), rand(B, H_kv, N, d)
+    o, lse = orc.attention_fwd(q, k, v, True, 0.3)
+    od, lsed = orc.attention_decode(q[:, :, -1], k, v, np.array([N]), 0.3)
+    np.testing.assert_allclose(od, o[:, :, -1], atol=1e-13)
+    np.testing.assert_allclose(lsed, lse[:, :, -1], atol=1e-13)
+
+
+# --------------------------------------------------------------- backward ---
+
+def torch_grads(q, k, v, dout, causal, scale):
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).requires_grad_(True) for x in (q, k, v))
+    g = qt.shape[1] // kt.shape[1]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(g, 1), vt.repeat_interleave(g, 1), is_causal=causal, scale=scale)
+    o.backward(torch.from_numpy(dout))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 64, 32), (2, 4, 2, 23, 8), (1, 4, 1, 17, 16)])
+def test_bwd_matches_torch_autograd(B, H, H_kv, N, d, causal):
+    q, k, v, do = rand(B, H, N, d), rand(B, H_kv, N, d), rand(B, H_kv, N, d), rand(B, H, N, d)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv, o, lse = orc.attention_bwd(q, k, v, do, causal, scale)
+    tq, tk, tv = torch_grads(q, k, v, do, causal, scale)
+    np.testing.assert_allclose(dq, tq, atol=1e-12)
+    np.testing.assert_allclose(dk, tk, atol=1e-12)
+    np.testing.assert_allclose(dv, tv, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (2, 1)])
+def test_bwd_finite_differences(causal, H, H_kv):
+    N, d, scale, h = 9, 4, 0.7, 1e-6
+    q, k, v, do = rand(1, H, N, d), rand(1, H_kv, N, d), rand(1, H_kv, N, d), rand(1, H, N, d)
+    dq, dk, dv, _, _ = orc.attention_bwd(q, k, v, do, causal, scale)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(orc.attention_fwd(q_, k_, v_, causal, scale)[0] * do))
+
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{k_ + "_": a for k_, a in args_p.items()})
+                        - loss(**{k_ + "_": a for k_, a in args_m.items()})) / (2 * h)
+        err = np.max(np.abs(num - grad)) / max(1.0, np.max(np.abs(grad)))
+        assert err < 1e-7, (name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_sum_invariants(causal):
+    N, d = 80, 16
+    q, k, v, do = rand(2, 2, N, d), rand(2, 2, N, d), rand(2, 2, N, d), rand(2, 2, N, d)
+    dq, dk, dv, o, lse = orc.attention_bwd(q, k, v, do, causal, 0.25)
+    # rows of dS sum to zero, so the key gradients sum to zero over keys
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    # rows of P sum to one, so the value gradients sum to the upstream gradient
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+
+
+def test_bwd_constant_v_and_zero_scale():
+    N, d = 30, 8
+    q, k, do = rand(1, 2, N, d), rand(1, 2, N, d), rand(1, 2, N, d)
+    v = np.broadcast_to(rand(d), (1, 2, N, d)).copy()
+    dq, dk, dv, _, _ = orc.attention_bwd(q, k, v, do, True, 0.4)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-13)
+    v2 = rand(1, 2, N, d)
+    dq, dk, dv, _, _ = orc.attention_bwd(q, k, v2, do, False, 0.0)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dv, np.broadcast_to(do.mean(axis=2, keepdims=True), dv.shape) * 1.0, atol=1e-13)
+
+
+def test_bwd_causal_last_key():
+    N, d, scale = 25, 8, 0.35
+    q, k, v, do = rand(1, 1, N, d), rand(1, 1, N, d), rand(1, 1, N, d), rand(1, 1, N, d)
+    dq, dk, dv, o, lse = orc.attention_bwd(q, k, v, do, True, scale)
+    # only the last query sees the last key: dV_{N-1} = p_{N-1,N-1} dO_{N-1}
+    p_last = math.exp(scale * float(q[0, 0, -1] @ k[0, 0, -1]) - lse[0, 0, -1])
+    np.testing.assert_allclose(dv[0, 0, -1], p_last * do[0, 0, -1], atol=1e-14)
