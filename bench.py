@@ -1,0 +1,268 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one forward + backward pass (attn_fwd then attn_bwd, all forward and backward kernels)
+of causal bf16 attention over the [B=2, H=16, N=4096, d=128] synthetic batch, inputs resident in
+HBM before timing starts. The decode kernels and the two 4k prefill forwards are timed as extra
+legs in the same run and reported beside the step. Kernel durations come from HIP events that
+the library records on its launch stream around every kernel while its timer is enabled.
+
+Output: one JSON line on stdout (rank 0), with the roofline of the dominant kernel and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--legs/--no-legs]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd/bwd TFLOP/s and decode HBM GB/s, % of MI355X roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", dest="legs", action="store_true", default=True)
+    ap.add_argument("--no-legs", dest="legs", action="store_false")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_stats(lib, before=None):
+    rec = lib.timing_read()
+    return {k: {"launches": n, "avg_ms": ms / n if n else None, "total_ms": ms} for k, (n, ms) in rec.items()}
+
+
+def time_region(torch, lib, fn, steps):
+    """Runs fn() `steps` times between synchronisations; returns (wall seconds, kernel stats)."""
+    lib.timing_reset()
+    torch.cuda.synchronize()
+    lib.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.timing_enable(False)
+    stats = kernel_stats(lib)
+    lib.timing_reset()
+    return t1 - t0, stats
+
+
+def cpu_baseline(w, target_s):
+    """The fp64 oracle's forward+backward on whole heads of the same workload until ~target_s elapse."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as orc
+    from roofline_attention_amd import inputs as I
+    from roofline_attention_amd import ledger as L
+
+    t = I.make_prefill(w, with_dout=True)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, elapsed = 0, 0.0
+    while done < len(heads) and (elapsed < target_s or done == 0):
+        b, h = heads[done]
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        args = [I.to_f64(t[n][sl]) for n in ("q", "k", "v", "do")]
+        t0 = time.perf_counter()
+        orc.attention_bwd(*args, w.causal, w.scale)  # also computes O and LSE (the forward)
+        elapsed += time.perf_counter() - t0
+        done += 1
+    flops = done * (L.fwd_flops(1, 1, w.N, w.d, w.causal) + L.bwd_flops(1, 1, w.N, w.d, w.causal))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, fp64 numpy forward+backward "
+                  f"with explicit S, {elapsed:.2f} s wall; algorithmic FLOPs (causal halved) / time",
+        "host": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build runs on a single "
+              f"MI355X and has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from roofline_attention_amd import binding as lib
+    from roofline_attention_amd import inputs as I
+    from roofline_attention_amd import ledger as L
+
+    torch.cuda.set_device(0)
+    w = I.WORKLOADS["fwdbwd_4k_causal"]
+    log(f"[bench] inputs {w}")
+    t = {k: x.cuda() for k, x in I.make_prefill(w, with_dout=True).items()}
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    ws = torch.empty(lib.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+
+    def step():
+        lib.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        lib.bwd(q, k, v, o, do, lse, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps")
+    wall, stats = time_region(torch, lib, step, a.steps)
+    ms_per_step = wall / a.steps * 1e3
+    step_flops = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal) + L.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    value = step_flops / (wall / a.steps) / 1e12
+    log(f"[bench] step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s")
+
+    # Algorithmic work per launch of each kernel of the step. The backward's five products are
+    # assigned where they are first computed: S, dP, dV, dK in the key-major kernel, dQ in the
+    # query-major kernel; the preprocess is HBM-bound (reads O and dO, writes D).
+    Nsq = w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    work = {
+        "fwd_bf16_d128_causal": ("mfma", 4.0 * Nsq),
+        "bwd_dkdv_d128_causal": ("mfma", 8.0 * Nsq),
+        "bwd_dq_d128_causal": ("mfma", 2.0 * Nsq),
+        "bwd_pre_d128": ("hbm", 2.0 * 2 * w.B * w.H * w.N * w.d + 4.0 * w.B * w.H * w.N),
+    }
+    kernels = {}
+    for name, st in stats.items():
+        kind, amount = work.get(name, (None, None))
+        ent = dict(st)
+        if kind == "mfma" and st["avg_ms"]:
+            ent["tflops"] = amount / (st["avg_ms"] * 1e-3) / 1e12
+            ent["frac_of_peak"] = ent["tflops"] / L.PEAK_BF16_TFLOPS
+        elif kind == "hbm" and st["avg_ms"]:
+            ent["gbs"] = amount / (st["avg_ms"] * 1e-3) / 1e9
+            ent["frac_of_peak"] = ent["gbs"] / L.PEAK_HBM_GBS
+        kernels[name] = ent
+    dom = max(stats, key=lambda n: stats[n]["total_ms"])
+    kind, amount = work[dom]
+    avg_s = stats[dom]["avg_ms"] * 1e-3
+    if kind == "mfma":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": amount / avg_s / 1e12, "peak": L.PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": amount / avg_s / 1e9, "peak": L.PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["avg_ms"] = stats[dom]["avg_ms"]
+    roof["algorithmic_per_launch"] = amount
+
+    legs = {}
+    if a.legs:
+        del q, k, v, do, o, lse, dq, dk, dv, ws, t
+        torch.cuda.empty_cache()
+        legs = run_legs(torch, lib, I, L)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, a.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), per-(tensor,batch,head) numpy PCG64 streams, bf16 RNE)",
+        "config": {"workload": "causal bf16 attention forward+backward B=2 H=16 N=4096 d=128 (fp32 grads)",
+                   "global_batch": w.B, "heads": w.H, "seq_len": w.N, "head_dim": w.d, "causal": True,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "legs": legs,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_legs(torch, lib, I, L, reps=20):
+    """Extra legs: the 4k prefill forward (causal and not), the 1k causal prefill, GQA decode."""
+    legs = {}
+    for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
+        w = I.WORKLOADS[name]
+        t = {k: x.cuda() for k, x in I.make_prefill(w, with_dout=False).items()}
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        fn = lambda: lib.fwd(t["q"], t["k"], t["v"], w.causal, w.scale, out=o, lse=lse)  # noqa: E731
+        for _ in range(3):
+            fn()
+        wall, stats = time_region(torch, lib, fn, reps)
+        (kname, st), = stats.items()
+        fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
+        legs[name] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": fl / (st["avg_ms"] * 1e-3) / 1e12,
+                      "frac_of_peak": fl / (st["avg_ms"] * 1e-3) / 1e12 / L.PEAK_BF16_TFLOPS,
+                      "wall_ms_per_call": wall / reps * 1e3}
+        log(f"[bench] leg {name}: {legs[name]['avg_ms']:.3f} ms, {legs[name]['tflops']:.1f} TFLOP/s")
+        del t, o, lse
+        torch.cuda.empty_cache()
+
+    w = I.WORKLOADS["decode_gqa"]
+    t = I.make_decode(w)
+    lens = t["kv_len"].numpy().tolist()
+    t = {k: x.cuda() for k, x in t.items()}
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(lib.decode_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # larger than the 256 MB last-level cache
+    fn = lambda: lib.decode(t["q"], t["k"], t["v"], t["kv_len"], w.scale, out=o, lse=lse, workspace=wsd)  # noqa
+    for _ in range(3):
+        fn()
+    # cold: the cache flush runs outside the timed kernels
+    lib.timing_reset()
+    lib.timing_enable(True)
+    for _ in range(reps):
+        lib.timing_enable(False)
+        flush.zero_()
+        lib.timing_enable(True)
+        fn()
+    torch.cuda.synchronize()
+    lib.timing_enable(False)
+    stats = kernel_stats(lib)
+    lib.timing_reset()
+    nbytes = L.decode_bytes(w.H, w.H_kv, w.d, 2, lens)
+    total_ms = sum(s["avg_ms"] for s in stats.values())
+    split = [n for n in stats if n.startswith("decode_split")][0]
+    legs["decode_gqa"] = {
+        "kernels": {n: s["avg_ms"] for n, s in stats.items()},
+        "compulsory_bytes": nbytes,
+        "gbs_split_kernel": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9,
+        "gbs_both_kernels": nbytes / (total_ms * 1e-3) / 1e9,
+        "frac_of_peak_split": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9 / L.PEAK_HBM_GBS,
+        "cache": "cold (1 GiB buffer zeroed before each call, outside the timed kernels)",
+        "tflops": L.decode_flops(w.H, w.d, lens) / (total_ms * 1e-3) / 1e12,
+    }
+    log(f"[bench] leg decode_gqa: {total_ms:.3f} ms, {legs['decode_gqa']['gbs_both_kernels']:.0f} GB/s")
+    return legs
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) exact-attention library libroofattn.so.
+ *
+ * Operation: exact scaled-dot-product attention, O = softmax(scale * Q K^T [+ causal mask]) V,
+ * as defined in "Why Fast GPUs Still Wait for Memory", section "Attention from first principles"
+ * (S = Q K^T, P = softmax(S), O = P V), computed by fused tiled kernels that keep S and P on chip
+ * (same page, section "FlashAttention is an IO algorithm"). The score factor `scale` is a free
+ * argument (the page writes S = Q K^T without it; callers normally pass 1/sqrt(d)).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (memory of the current HIP device), 16-byte aligned,
+ *     densely packed row-major with the head dimension d contiguous:
+ *       Q, O, dO, dQ : [B, H,    N, d]       K, V, dK, dV : [B, H_kv, N, d]
+ *       LSE          : [B, H, N] float32, natural-log log-sum-exp of each score row.
+ *   - Grouped-query attention: H must be a multiple of H_kv; query head h reads KV head
+ *     h / (H / H_kv) (contiguous groups), as in "Why Fast GPUs Still Wait for Memory",
+ *     section "Attention III - KV cache, GQA, MLA" (group size g = h / h_kv).
+ *   - causal != 0 keeps key j for query i only when j <= i (lower triangle with the diagonal;
+ *     same page, note "causal masking is not an optimisation here").
+ *   - d must be 64 or 128. N >= 1; N * d must not exceed 2^30.
+ *   - Ownership: the caller allocates and frees every buffer, including workspaces. The library
+ *     allocates no device memory, keeps no pointer after a call returns, and holds no state except
+ *     the opt-in kernel timer below.
+ *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without waiting. Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Errors: every argument check runs before any launch; a failing check enqueues nothing and
+ *     returns a non-zero attn_status. attn_last_error() then describes it (per calling thread).
+ *     Output buffers must not overlap input buffers (checked by address range).
+ */
+#ifndef ROOFLINE_ATTENTION_ATTN_H
+#define ROOFLINE_ATTENTION_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, overlap, H % H_kv != 0 */
+  ATTN_ERR_UNSUPPORTED = 2, /* d not in {64, 128}, dtype not supported by this entry point */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the size query returns */
+  ATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum attn_dtype {
+  ATTN_F32 = 0,  /* float32 storage and arithmetic */
+  ATTN_BF16 = 1  /* bfloat16 storage, float32 accumulation */
+} attn_dtype;
+
+/* Version of this ABI; bumped on any signature or semantic change. */
+int attn_abi_version(void);
+
+/* Static name of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* Message describing the last failing call made by this thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Forward pass (prefill): O = softmax(scale * Q K^T [causal]) V and, if lse != NULL, LSE.
+ *   dtype ATTN_F32 : q, k, v, o are float32.
+ *   dtype ATTN_BF16: q, k, v, o are bfloat16 (o rounded to nearest even); lse is float32.
+ * The online-softmax recurrence (running row maximum and normaliser, output rescaled as each
+ * K/V block arrives) follows "Why Fast GPUs Still Wait for Memory", section "FlashAttention is an
+ * IO algorithm"; it equals the two-pass softmax up to rounding.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int H_kv, int N, int d, int causal, float scale,
+                     int dtype, void* stream);
+
+/*
+ * Decode: one query token per (sequence, head) against a KV cache, the regime of
+ * "Why Fast GPUs Still Wait for Memory", section "Attention III - KV cache, GQA, MLA"
+ * (I = 2g/s, memory-bound). The key range of each sequence is split across workgroups and a
+ * second kernel merges the partial (max, sum, output) triples ("M4.2 - GPU Execution Model for
+ * Transformer Kernels", section 0x08: split-K needs an extra reduction).
+ *   q [B, H, d] bf16; k_cache, v_cache [B, H_kv, N_cap, d] bf16; o [B, H, d] bf16;
+ *   lse [B, H] float32 or NULL; kv_len [B] int32 DEVICE array, sequence b attends to cache rows
+ *   0 .. kv_len[b]-1 and never reads rows at or beyond kv_len[b]. Values are clamped to
+ *   [0, N_cap] on the device; kv_len[b] == 0 yields o = 0 and lse = -inf for that sequence.
+ *   `causal` is accepted for signature symmetry and ignored: the single query follows every key.
+ *   workspace: device buffer of at least attn_decode_workspace_size(B, H, N_cap, d) bytes,
+ *   16-byte aligned, contents need no initialisation; it is scratch owned by the caller.
+ * dtype must be ATTN_BF16.
+ */
+size_t attn_decode_workspace_size(int B, int H, int N_cap, int d);
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, int causal,
+                        float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass: gradients of L = sum(O * dO) with respect to Q, K and V, recomputing the scores
+ * from Q and K instead of reading a stored N x N matrix ("Why Fast GPUs Still Wait for Memory",
+ * section "FlashAttention is an IO algorithm": the backward recomputes S). Every gradient element
+ * is written by exactly one workgroup and no atomics are used (the race-free-by-construction rule
+ * of the MoA paper, "Validating Memory-Optimal Transformer Kernels on Real Hardware", section 4.5).
+ *   q, k, v, o, dout: bf16 in the layouts above; o and lse must come from attn_fwd on the same
+ *   q, k, v, causal and scale. dq [B,H,N,d], dk, dv [B,H_kv,N,d]: float32, fully overwritten.
+ *   workspace: at least attn_bwd_workspace_size(B, H, N, d) bytes, 16-byte aligned, scratch.
+ * dtype must be ATTN_BF16. H_kv must equal H (grouped-query backward is not provided).
+ */
+size_t attn_bwd_workspace_size(int B, int H, int N, int d);
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* dq, float* dk, float* dv,
+                     int B, int H, int H_kv, int N, int d, int causal, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Opt-in kernel timer for measurement harnesses ("M4.2 - GPU Execution Model for Transformer
+ * Kernels", section 0x0B: device-side timing with events on the launching stream). While enabled,
+ * every kernel the library launches is bracketed by a pair of HIP events on its own stream.
+ * attn_timing_get synchronises on the recorded events and returns, for the index-th kernel name
+ * seen since the last reset, its static name, launch count and summed duration in milliseconds.
+ * Not for concurrent use from several threads.
+ */
+attn_status attn_timing_enable(int on);
+attn_status attn_timing_reset(void);
+int attn_timing_count(void);
+attn_status attn_timing_get(int index, const char** name, long long* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROOFLINE_ATTENTION_ATTN_H */

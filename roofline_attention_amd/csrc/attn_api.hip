@@ -1,0 +1,276 @@
+// C-ABI layer of libroofattn.so: argument validation, dispatch to the kernel launchers, status
+// strings and the opt-in kernel timer. Every check runs before any HIP call, so a rejected call
+// has no side effects on the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string t_last_error;
+
+attn_status fail(attn_status st, const char* msg) {
+  t_last_error = msg;
+  return st;
+}
+
+attn_status ok() {
+  t_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Range a, Range b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Common shape checks; returns ATTN_OK or the failing status (message already set).
+attn_status check_shape(int B, int H, int H_kv, int N, int d, float scale) {
+  if (B < 1 || H < 1 || H_kv < 1 || N < 1) return fail(ATTN_ERR_INVALID_ARG, "B, H, H_kv and N must be >= 1");
+  if (H % H_kv != 0) return fail(ATTN_ERR_INVALID_ARG, "H must be a multiple of H_kv");
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dimension d must be 64 or 128");
+  if ((long long)N * d > (1LL << 30)) return fail(ATTN_ERR_INVALID_ARG, "N * d exceeds 2^30");
+  if (B > 65535 || H > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and H must be <= 65535");
+  if (!isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "scale must be finite");
+  return ATTN_OK;
+}
+
+attn_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return ok();
+  t_last_error = std::string("HIP launch error: ") + hipGetErrorString(e);
+  return ATTN_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------- timer ----
+
+struct TimerRecord {
+  std::string name;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  long long launches = 0;
+  double total_ms = 0.0;
+};
+
+std::mutex g_mu;
+bool g_timing = false;
+std::vector<TimerRecord> g_records;
+std::vector<hipEvent_t> g_free_events;
+
+hipEvent_t take_event() {
+  if (!g_free_events.empty()) {
+    hipEvent_t e = g_free_events.back();
+    g_free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+TimerRecord& record_for(const char* name) {
+  for (auto& r : g_records)
+    if (r.name == name) return r;
+  g_records.push_back(TimerRecord{});
+  g_records.back().name = name;
+  return g_records.back();
+}
+
+attn_status drain_locked() {
+  for (auto& r : g_records) {
+    for (auto& pr : r.pending) {
+      if (hipEventSynchronize(pr.second) != hipSuccess) return fail(ATTN_ERR_HIP, "event synchronize failed");
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+        return fail(ATTN_ERR_HIP, "event elapsed time failed");
+      r.total_ms += ms;
+      r.launches += 1;
+      g_free_events.push_back(pr.first);
+      g_free_events.push_back(pr.second);
+    }
+    r.pending.clear();
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+namespace ra {
+
+TimedScope::TimedScope(const char* name, hipStream_t stream) : name_(name), stream_(stream), start_(nullptr) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_timing) return;
+  hipEvent_t e = take_event();
+  if (e != nullptr && hipEventRecord(e, stream_) == hipSuccess) start_ = e;
+}
+
+TimedScope::~TimedScope() {
+  if (start_ == nullptr) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipEvent_t e = take_event();
+  if (e == nullptr || hipEventRecord(e, stream_) != hipSuccess) return;
+  record_for(name_).pending.emplace_back(static_cast<hipEvent_t>(start_), e);
+}
+
+}  // namespace ra
+
+extern "C" {
+
+int attn_abi_version(void) { return 1; }
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_ERR_UNKNOWN";
+  }
+}
+
+const char* attn_last_error(void) { return t_last_error.c_str(); }
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                     int N, int d, int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  attn_status st = check_shape(B, H, H_kv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dtype must be ATTN_F32 or ATTN_BF16");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t es = dtype == ATTN_F32 ? 4 : 2;
+  const size_t qb = (size_t)B * H * N * d * es, kb = (size_t)B * H_kv * N * d * es, lb = (size_t)B * H * N * 4;
+  const Range rq{q, qb}, rk{k, kb}, rv{v, kb}, ro{o, qb}, rl{lse, lse ? lb : 0};
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) || overlap(rl, rk) ||
+      overlap(rl, rv) || overlap(rl, ro))
+    return fail(ATTN_ERR_INVALID_ARG, "outputs overlap inputs or each other");
+  const long long tiles = (long long)((N + 63) / 64) * H * B;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_F32)
+    return hip_status(ra::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                         static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, H_kv, N, d,
+                                         causal != 0, scale, s));
+  return hip_status(ra::launch_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0, scale, s));
+}
+
+size_t attn_decode_workspace_size(int B, int H, int N_cap, int d) {
+  if (B < 1 || H < 1 || N_cap < 1 || (d != 64 && d != 128)) return 0;
+  return ra::decode_workspace_bytes(B, H, N_cap, d);
+}
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, int causal, float scale,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)causal;
+  if (!q || !k_cache || !v_cache || !o || !kv_len)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and kv_len must be non-null");
+  attn_status st = check_shape(B, H, H_kv, N_cap, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports ATTN_BF16 only");
+  const int G = H / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ATTN_ERR_UNSUPPORTED, "decode group size H/H_kv must be 1, 2, 4 or 8");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(kv_len) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "kv_len and lse must be 4-byte aligned");
+  const size_t need = ra::decode_workspace_bytes(B, H, N_cap, d);
+  if (workspace == nullptr || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "decode workspace too small");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t qb = (size_t)B * H * d * 2, cb = (size_t)B * H_kv * N_cap * d * 2;
+  const Range rq{q, qb}, rk{k_cache, cb}, rv{v_cache, cb}, ro{o, qb}, rl{lse, lse ? (size_t)B * H * 4 : 0},
+      rw{workspace, need}, rn{kv_len, (size_t)B * 4};
+  const Range outs[] = {ro, rl, rw};
+  const Range ins[] = {rq, rk, rv, rn};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
+  if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw))
+    return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
+  return hip_status(ra::launch_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return ra::bwd_workspace_bytes(B, H, N, d);
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     float* dq, float* dk, float* dv, int B, int H, int H_kv, int N, int d, int causal, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "all tensor pointers must be non-null");
+  attn_status st = check_shape(B, H, H_kv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "backward supports ATTN_BF16 only");
+  if (H_kv != H) return fail(ATTN_ERR_UNSUPPORTED, "backward requires H_kv == H");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t need = ra::bwd_workspace_bytes(B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "backward workspace too small");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const long long tiles = (long long)((N + 127) / 128) * H * B;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  const size_t tb = (size_t)B * H * N * d * 2, gb = (size_t)B * H * N * d * 4, lb = (size_t)B * H * N * 4;
+  const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dout, tb}, {lse, lb}};
+  const Range outs[] = {{dq, gb}, {dk, gb}, {dv, gb}, {workspace, need}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
+  return hip_status(ra::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal != 0, scale, workspace,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = on != 0;
+  return ok();
+}
+
+attn_status attn_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  attn_status st = drain_locked();
+  g_records.clear();
+  return st == ATTN_OK ? ok() : st;
+}
+
+int attn_timing_count(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return (int)g_records.size();
+}
+
+attn_status attn_timing_get(int index, const char** name, long long* launches, double* total_ms) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (index < 0 || index >= (int)g_records.size()) return fail(ATTN_ERR_INVALID_ARG, "timer index out of range");
+  attn_status st = drain_locked();
+  if (st != ATTN_OK) return st;
+  const TimerRecord& r = g_records[index];
+  if (name) *name = r.name.c_str();
+  if (launches) *launches = r.launches;
+  if (total_ms) *total_ms = r.total_ms;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Device-side building blocks shared by the gfx950 attention kernels: vector types, bf16
+// conversion, the MFMA wrappers and wave-level exchanges.
+//
+// MFMA register layouts used throughout (CDNA3/CDNA4 matrix-core conventions, wave64):
+//   v_mfma_f32_32x32x16_bf16, D(32x32) += A(32x16) * B(16x32):
+//     A: lane l holds row  (l % 32) and 8 consecutive k values of k-group (l / 32);
+//     B: lane l holds col  (l % 32) and the same 8 k values of k-group (l / 32);
+//     D: lane l holds col  (l % 32) and rows 8*(r/4) + 4*(l/32) + (r%4) for r = 0..15.
+// Only the row/col placement of A, B and D is relied on. Which physical k an element slot
+// carries does not matter as long as A and B use the same slot for the same logical k, which
+// every kernel here guarantees by construction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// float -> bf16, round to nearest even (gfx950 lowers this to v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane gets the total.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));  // xor 1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));  // xor 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true)); // half mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true)); // mirror
+  return x;
+}
+
+// Maps a linear workgroup id so that consecutive logical work items run on the same XCD.
+// Workgroups are handed to the 8 XCDs round-robin, so hardware slot L lands on XCD L % 8;
+// giving XCD x the logical range [x*per, (x+1)*per) keeps work that shares K/V in one L2.
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+  constexpr int kXcd = 8;
+  if (total % kXcd != 0) return L;
+  const int per = total / kXcd;
+  return (L % kXcd) * per + L / kXcd;
+}
+
+}  // namespace ra

@@ -1,0 +1,48 @@
+// Host-side launchers of the attention kernels (internal to libroofattn.so).
+// Each launcher assumes its arguments were validated by the C-ABI layer and returns the
+// hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Brackets one kernel launch with timing events when the opt-in timer is enabled.
+class TimedScope {
+ public:
+  TimedScope(const char* name, hipStream_t stream);
+  ~TimedScope();
+  TimedScope(const TimedScope&) = delete;
+  TimedScope& operator=(const TimedScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  void* start_;
+};
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int H_kv, int N, int d, bool causal, float scale,
+                           hipStream_t stream);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int H, int H_kv, int N, int d, bool causal, float scale,
+                          hipStream_t stream);
+
+// Decode split size (keys per workgroup) and workspace layout: per (b, h, split) a record of
+// d + 2 floats {m, l, o[0..d)} (m in log2 units of the scaled score).
+constexpr int kDecodeSplit = 256;
+size_t decode_workspace_bytes(int B, int H, int N_cap, int d);
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* lse,
+                         const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d,
+                         float scale, void* ws, hipStream_t stream);
+
+size_t bwd_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* dq, float* dk, float* dv,
+                      int B, int H, int N, int d, bool causal, float scale, void* ws,
+                      hipStream_t stream);
+
+}  // namespace ra

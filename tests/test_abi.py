@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and its
+argument validation rejects bad calls before any HIP work is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+LIB = os.path.join(ROOT, "roofline_attention_amd", "libroofattn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libroofattn.so not built")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from roofline_attention_amd import binding
+    return binding.raw()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_signatures_cover_the_header():
+    from roofline_attention_amd import binding
+    assert sorted(binding.SIGNATURES) == declared_functions()
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_abi_version() == 1
+    assert lib.attn_status_string(OK) == b"ATTN_OK"
+    assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
+    assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
+
+
+# Fake, well-aligned, non-overlapping device addresses: validation rejects each call below before
+# any HIP call, so the addresses are never dereferenced.
+BASE = 1 << 40
+GAP = 1 << 34
+
+
+def addr(i):
+    return ctypes.c_void_p(BASE + i * GAP)
+
+
+def fwd(lib, B=1, H=2, H_kv=2, N=128, d=64, causal=0, scale=0.125, dtype=BF16, ptrs=None):
+    p = ptrs or [addr(i) for i in range(5)]
+    return lib.attn_fwd(p[0], p[1], p[2], p[3], p[4], B, H, H_kv, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(H=3, H_kv=2), INVALID), (dict(N=0), INVALID), (dict(B=0), INVALID), (dict(H_kv=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(N=1 << 24, d=128), INVALID),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, want):
+    assert fwd(lib, **kw) == want
+    assert lib.attn_last_error() != b""
+
+
+def test_fwd_rejects_null_misaligned_and_overlapping(lib):
+    p = [addr(i) for i in range(5)]
+    assert fwd(lib, ptrs=[None] + p[1:]) == INVALID
+    mis = list(p)
+    mis[1] = ctypes.c_void_p(BASE + GAP + 8)
+    assert fwd(lib, ptrs=mis) == INVALID
+    ov = list(p)
+    ov[3] = ctypes.c_void_p(BASE + 64)  # output inside q
+    assert fwd(lib, ptrs=ov) == INVALID
+    ov = list(p)
+    ov[4] = ctypes.c_void_p(BASE + 3 * GAP + 16)  # lse inside o
+    assert fwd(lib, ptrs=ov) == INVALID
+
+
+def test_decode_validation(lib):
+    p = [addr(i) for i in range(7)]
+    ws_need = lib.attn_decode_workspace_size(64, 32, 8192, 128)
+    assert ws_need == 64 * 32 * 32 * (128 + 4) * 4
+
+    def call(B=64, H=32, H_kv=8, N_cap=8192, d=128, dtype=BF16, ws=p[6], ws_bytes=ws_need, kv=p[5]):
+        return lib.attn_decode(p[0], p[1], p[2], p[3], p[4], kv, B, H, H_kv, N_cap, d, 0, 0.088, dtype, ws,
+                               ws_bytes, None)
+
+    assert call(ws_bytes=ws_need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(H=48, H_kv=4) == UNSUPPORTED  # group of 12
+    assert call(H=30) == INVALID
+    assert call(kv=None) == INVALID
+    assert call(d=80) == UNSUPPORTED
+    assert lib.attn_decode_workspace_size(1, 1, 1, 96) == 0
+
+
+def test_bwd_validation(lib):
+    p = [addr(i) for i in range(11)]
+    need = lib.attn_bwd_workspace_size(2, 16, 4096, 128)
+    assert need == 2 * 16 * 4096 * 4
+
+    def call(H=16, H_kv=16, dtype=BF16, ws_bytes=need, lse=p[5]):
+        return lib.attn_bwd(p[0], p[1], p[2], p[3], p[4], lse, p[6], p[7], p[8], 2, H, H_kv, 4096, 128, 1, 0.088,
+                            dtype, p[9], ws_bytes, None)
+
+    assert call(ws_bytes=need - 4) == WORKSPACE
+    assert call(H_kv=4) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(lse=None) == INVALID
+
+
+def test_timer_without_launches(lib):
+    assert lib.attn_timing_reset() == OK
+    assert lib.attn_timing_count() == 0
+    assert lib.attn_timing_get(0, None, None, None) == INVALID

@@ -1,0 +1,255 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same seeded inputs.
+
+Tolerances (max abs error per output tensor): 1e-5 on the float32 path, 2e-2 on the bf16 path
+with fp32 accumulation. Small cases are compared element by element at sizes that span several
+tiles and a ragged tail; the full-size workloads are compared on every element the oracle can
+afford (all of the 1k causal prefill and the decode batch) or on sampled rows and heads.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as orc
+from roofline_attention_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def f64(t):
+    return I.to_f64(t)
+
+
+def max_err(gpu, ref):
+    return float(np.max(np.abs(f64(gpu) - ref))) if ref.size else 0.0
+
+
+def run_fwd(lib, w, causal=None):
+    t = I.make_prefill(w, with_dout=False)
+    causal = w.causal if causal is None else causal
+    o, lse = lib.fwd(dev(t["q"]), dev(t["k"]), dev(t["v"]), causal, w.scale)
+    torch.cuda.synchronize()
+    return t, o.cpu(), lse.cpu()
+
+
+# ---------------------------------------------------------------------------- forward ----
+
+def test_tiny_f32_workload(lib):
+    w = I.WORKLOADS["tiny_f32"]
+    t, o, lse = run_fwd(lib, w)
+    ro, rl = orc.attention_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), w.causal, w.scale)
+    assert max_err(o, ro) <= TOL_F32
+    assert max_err(lse, rl) <= TOL_F32
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 333, 64), (2, 4, 2, 77, 128), (1, 3, 1, 1, 64),
+                                           (1, 2, 2, 200, 128)])
+def test_f32_shapes(lib, B, H, H_kv, N, d, causal):
+    w = I.Workload("f32_case", "fwd", B, H, H_kv, N, d, "f32", causal, seed=11)
+    t, o, lse = run_fwd(lib, w)
+    ro, rl = orc.attention_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), causal, w.scale)
+    assert max_err(o, ro) <= TOL_F32
+    assert max_err(lse, rl) <= TOL_F32
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 333, 128), (1, 2, 2, 333, 64), (2, 8, 2, 200, 128),
+                                           (1, 4, 1, 65, 64), (1, 2, 2, 1, 128), (1, 1, 1, 129, 128),
+                                           (1, 2, 2, 512, 64)])
+def test_bf16_shapes(lib, B, H, H_kv, N, d, causal):
+    w = I.Workload("bf16_case", "fwd", B, H, H_kv, N, d, "bf16", causal, seed=12)
+    t, o, lse = run_fwd(lib, w)
+    ro, rl = orc.attention_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), causal, w.scale)
+    assert max_err(o, ro) <= TOL_BF16
+    assert max_err(lse, rl) <= TOL_BF16
+
+
+def test_prefill_causal_1k_full(lib):
+    w = I.WORKLOADS["prefill_causal_1k"]
+    t, o, lse = run_fwd(lib, w)
+    ro, rl = orc.attention_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), w.causal, w.scale)
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    print(f"prefill_causal_1k: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
+def sample_rows(B, H, N, n_rand, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [(0, 0, 0), (0, 0, 1), (B - 1, H - 1, N - 1), (0, H - 1, 127), (0, H - 1, 128), (B - 1, 0, 63),
+             (B - 1, 0, 64), (0, 1, N // 2), (B - 1, H // 2, N - 129)]
+    rnd = np.stack([rng.integers(0, B, n_rand), rng.integers(0, H, n_rand), rng.integers(0, N, n_rand)], 1)
+    return np.concatenate([np.array(fixed), rnd])
+
+
+@pytest.mark.parametrize("name", ["prefill_4k_causal", "prefill_4k"])
+def test_prefill_4k_sampled_rows_and_heads(lib, name):
+    w = I.WORKLOADS[name]
+    t, o, lse = run_fwd(lib, w)
+    q, k, v = f64(t["q"]), f64(t["k"]), f64(t["v"])
+    rows = sample_rows(w.B, w.H, w.N, 300, seed=3)
+    ro, rl = orc.attention_fwd_rows(q, k, v, w.causal, w.scale, rows)
+    og = f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lg = f64(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    # one whole head as well
+    rh, rhl = orc.attention_fwd(q[1:2, 31:32], k[1:2, 31:32], v[1:2, 31:32], w.causal, w.scale)
+    e = max(float(np.max(np.abs(og - ro))), float(np.max(np.abs(f64(o)[1:2, 31:32] - rh))))
+    el = max(float(np.max(np.abs(lg - rl))), float(np.max(np.abs(f64(lse)[1:2, 31:32] - rhl))))
+    print(f"{name}: max|dO|={e:.3e} max|dLSE|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_BF16
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_causal_row0_and_constant_v(lib):
+    w = I.Workload("inv", "fwd", 1, 2, 2, 300, 128, "bf16", True, seed=13)
+    t = I.make_prefill(w, with_dout=False)
+    o, lse = lib.fwd(dev(t["q"]), dev(t["k"]), dev(t["v"]), True, w.scale)
+    o = o.cpu()
+    # row 0 attends to key 0 only: P = 1 exactly, so O[0] = V[0] (bf16 round trip of V is exact)
+    assert torch.equal(o[:, :, 0], t["v"][:, :, 0])
+    cv = t["v"][:, :, :1].expand_as(t["v"]).contiguous()
+    o2, _ = lib.fwd(dev(t["q"]), dev(t["k"]), dev(cv), True, w.scale)
+    assert float((o2.cpu().float() - cv.float()).abs().max()) <= TOL_BF16
+
+
+def test_one_hot_selection(lib):
+    N, d = 256, 128
+    sel = torch.arange(N) % d
+    k = torch.zeros(1, 1, N, d)
+    k[0, 0, torch.arange(d), torch.arange(d)] = 1.0
+    q = torch.zeros(1, 1, N, d)
+    q[0, 0, torch.arange(N), sel] = 64.0
+    v = torch.from_numpy(I.normal_block(14, 2, 0, 0, (N, d))).view(1, 1, N, d)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    o, _ = lib.fwd(dev(q), dev(k), dev(v), False, 1.0)  # scale*c = 64 -> weight of others ~ N e^-64
+    assert float((o.cpu().float()[0, 0] - v.float()[0, 0, sel]).abs().max()) <= TOL_BF16
+
+
+def test_forward_is_deterministic(lib):
+    w = I.Workload("det", "fwd", 2, 4, 4, 520, 128, "bf16", True, seed=15)
+    t = I.make_prefill(w, with_dout=False)
+    q, k, v = dev(t["q"]), dev(t["k"]), dev(t["v"])
+    o1, l1 = lib.fwd(q, k, v, True, w.scale)
+    o2, l2 = lib.fwd(q, k, v, True, w.scale)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------- decode ----
+
+def decode_check(lib, w, kv_len=None, n_seq_check=None):
+    t = I.make_decode(w)
+    if kv_len is not None:
+        t = I.make_decode(w, nan_pad=False)
+        t["kv_len"] = torch.tensor(kv_len, dtype=torch.int32)
+        for b in range(w.B):
+            t["k"][b, :, kv_len[b]:] = float("nan")
+            t["v"][b, :, kv_len[b]:] = float("nan")
+    o, lse = lib.decode(dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["kv_len"]), w.scale)
+    o, lse = o.cpu(), lse.cpu()
+    q = f64(t["q"])
+    lens = t["kv_len"].numpy()
+    err_o = err_l = 0.0
+    seqs = range(w.B) if n_seq_check is None else range(min(w.B, n_seq_check))
+    for b in seqs:
+        n = int(lens[b])
+        kb = f64(t["k"][b:b + 1, :, :n])
+        vb = f64(t["v"][b:b + 1, :, :n])
+        ro, rl = orc.attention_decode(q[b:b + 1], kb, vb, np.array([n]), w.scale)
+        err_o = max(err_o, float(np.max(np.abs(f64(o[b:b + 1]) - ro))))
+        err_l = max(err_l, float(np.max(np.abs(f64(lse[b:b + 1]) - rl))))
+    return err_o, err_l
+
+
+def test_decode_gqa_full_workload(lib):
+    w = I.WORKLOADS["decode_gqa"]
+    eo, el = decode_check(lib, w)
+    print(f"decode_gqa: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
+@pytest.mark.parametrize("H,H_kv,d", [(8, 8, 128), (8, 4, 64), (16, 4, 128), (16, 2, 128), (8, 1, 64)])
+def test_decode_ragged_lengths(lib, H, H_kv, d):
+    w = I.Workload("dec", "decode", 7, H, H_kv, 1100, d, "bf16", False, seed=16, kv_lo=1, kv_hi=1100)
+    eo, el = decode_check(lib, w, kv_len=[1, 255, 256, 257, 512, 1099, 1100])
+    assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
+def test_decode_zero_length_is_defined(lib):
+    w = I.Workload("dec0", "decode", 2, 4, 4, 64, 128, "bf16", False, seed=17, kv_lo=1, kv_hi=64)
+    t = I.make_decode(w)
+    kv = torch.tensor([0, 5], dtype=torch.int32)
+    o, lse = lib.decode(dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(kv), w.scale)
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.isfinite(o[1].float()).all()
+
+
+# --------------------------------------------------------------------------- backward ----
+
+def bwd_case(lib, w):
+    t = I.make_prefill(w, with_dout=True)
+    q, k, v, do = dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["do"])
+    o, lse = lib.fwd(q, k, v, w.causal, w.scale)
+    dq, dk, dv = lib.bwd(q, k, v, o, do, lse, w.causal, w.scale)
+    torch.cuda.synchronize()
+    return t, o.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 128), (1, 2, 200, 128), (2, 2, 333, 64), (1, 1, 1, 128),
+                                      (1, 2, 65, 64)])
+def test_bwd_shapes(lib, B, H, N, d, causal):
+    w = I.Workload("bwd_case", "fwdbwd", B, H, H, N, d, "bf16", causal, seed=18)
+    t, o, dq, dk, dv = bwd_case(lib, w)
+    rdq, rdk, rdv, ro, _ = orc.attention_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), causal, w.scale)
+    errs = [max_err(o, ro), max_err(dq, rdq), max_err(dk, rdk), max_err(dv, rdv)]
+    assert max(errs) <= TOL_BF16, errs
+
+
+def test_fwdbwd_4k_causal_sampled_heads(lib):
+    w = I.WORKLOADS["fwdbwd_4k_causal"]
+    t, o, dq, dk, dv = bwd_case(lib, w)
+    worst = [0.0] * 4
+    for b, h in ((0, 0), (1, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rdq, rdk, rdv, ro, _ = orc.attention_bwd(f64(t["q"][sl]), f64(t["k"][sl]), f64(t["v"][sl]),
+                                                 f64(t["do"][sl]), w.causal, w.scale)
+        errs = [max_err(o[sl], ro), max_err(dq[sl], rdq), max_err(dk[sl], rdk), max_err(dv[sl], rdv)]
+        worst = [max(a, e) for a, e in zip(worst, errs)]
+    print(f"fwdbwd_4k_causal: max|dO|,|ddQ|,|ddK|,|ddV| = {worst}")
+    assert max(worst) <= TOL_BF16, worst
+    for x in (dq, dk, dv):
+        assert torch.isfinite(x).all()
+
+
+def test_bwd_is_deterministic(lib):
+    w = I.Workload("bdet", "fwdbwd", 1, 4, 4, 384, 128, "bf16", True, seed=19)
+    t = I.make_prefill(w, with_dout=True)
+    q, k, v, do = dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["do"])
+    o, lse = lib.fwd(q, k, v, True, w.scale)
+    a = lib.bwd(q, k, v, o, do, lse, True, w.scale)
+    b = lib.bwd(q, k, v, o, do, lse, True, w.scale)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_timer_reports_kernels(lib):
+    w = I.Workload("tm", "fwd", 1, 2, 2, 256, 128, "bf16", True, seed=20)
+    t = I.make_prefill(w, with_dout=False)
+    lib.timing_reset()
+    lib.timing_enable(True)
+    try:
+        for _ in range(3):
+            lib.fwd(dev(t["q"]), dev(t["k"]), dev(t["v"]), True, w.scale)
+    finally:
+        lib.timing_enable(False)
+    rec = lib.timing_read()
+    lib.timing_reset()
+    assert rec["fwd_bf16_d128_causal"][0] == 3 and rec["fwd_bf16_d128_causal"][1] > 0
