@@ -11,21 +11,23 @@
 //   * Scores are produced transposed, S^T = K Q^T (A = K rows from LDS, B = Q), so each lane holds
 //     one query row: the row max needs one v_permlane32_swap, and the probabilities leave the
 //     accumulator already in the B-operand layout of O^T = V^T P^T.
-//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4, no VGPR staging),
-//     double-buffered so the loads of tile j+1 overlap the math of tile j with one barrier per
-//     tile. Each wave instruction fills 1 KB of LDS in lane order, so bank conflicts are avoided by
-//     an XOR swizzle of the 16-byte chunks within a row instead of padding.
+//   * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds, no VGPR staging;
+//     the buffer range check zero-fills rows past the sequence end).
+//     Each wave instruction fills 1 KB of LDS in lane order, so bank conflicts are avoided by an
+//     XOR swizzle of the 16-byte chunks within a row instead of padding.
 //   * The V^T operand of O^T = V^T P^T comes from ds_read_b64_tr_b16, which transposes 16-bit
 //     elements across each 16-lane group, so V is never transposed in memory.
+//   * Software pipeline: while the softmax of tile j runs on the vector ALUs, the score MFMAs of
+//     tile j+1 are issued from the same basic block, so one wave keeps the matrix cores fed. K is
+//     therefore loaded one tile ahead of V (two LDS stages each, one barrier per tile).
 //   * The running maximum is only raised when a tile's maximum exceeds it by more than 8 (log2
 //     units); the numerator and the normaliser always share the same reference, so the result is
 //     unchanged while the output rescale is skipped on almost every tile.
-//   * Masks are evaluated only on tiles that cross the causal diagonal or the sequence end.
+//   * Masks are applied only on tiles that cross the causal diagonal or the sequence end.
 //   * Workgroup ids are remapped so the query tiles of one head run on one XCD (shared L2), and
 //     causal tiles run heaviest first to shorten the tail.
+#include <float.h>
 #include <math.h>
-
-#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -39,9 +41,8 @@ constexpr int FWD_THREADS = 256;
 constexpr float kLazyRescale = 8.0f;  // log2 units: P values stay below 2^8
 
 // LDS tiles: [2 stages][FWD_BC rows][HD] bf16, unpadded. The 16-byte chunk c of row r is stored
-// at chunk position c ^ swz(r): swz_k(r) = r mod CH spreads the 32 rows one MFMA A-operand read
-// touches over all banks; swz_v(r) = 2r mod CH does the same for the 4-row x 32-byte footprint
-// of a 16-lane transposed read.
+// at chunk position c ^ swz(r): swz_k spreads the 32 rows one MFMA A-operand read touches over
+// the banks; swz_v spreads the 4-row footprint of a transposed read (32 lanes per LDS cycle).
 template <int HD>
 struct FwdSmem {
   bf16 k[2][FWD_BC * HD];
@@ -51,17 +52,25 @@ struct FwdSmem {
 template <int HD>
 __device__ __forceinline__ int swz_k(int r) { return r & (HD / 8 - 1); }
 template <int HD>
-__device__ __forceinline__ int swz_v(int r) { return (2 * r) & (HD / 8 - 1); }
-
-typedef void __attribute__((address_space(3))) * lds_void_ptr;
-typedef const void __attribute__((address_space(1))) * global_void_ptr;
-
-// One 16-byte-per-lane direct load into LDS: lane i of the wave writes lds_block + 16 i.
-__device__ __forceinline__ void load_to_lds(const void* src, void* lds_block) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)lds_block, 16, 0, 0);
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (HD == 128) return 4 * (r & 3) + 2 * ((r >> 1) & 1);
+  else return (2 * r) & 7;
 }
 
+typedef void __attribute__((address_space(3))) * lds_void_ptr;
 typedef bf16x4 __attribute__((address_space(3))) * lds_bf16x4_ptr;
+
+// Buffer resource over `bytes` bytes from `base` (raw buffer, 32-bit byte offsets). Loads at or
+// beyond `bytes` return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// One 16-byte-per-lane direct load into LDS: lane i of the wave writes lds_block + 16 i with the
+// bytes at voffset of the resource (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset, void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds_block, 16, voffset, 0, 0, 0);
+}
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
@@ -82,6 +91,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   constexpr int KSTEPS = HD / 16;  // MFMA k-steps over the head dimension
   constexpr int CBLK = HD / 32;    // 32-wide head-dimension blocks of O^T
   constexpr int CHUNKS = HD / 8;   // 16-byte chunks per row
+  constexpr int RPI = 1024 / (HD * 2);   // rows per direct-load wave instruction
+  constexpr int BLOCKS = FWD_BC / RPI;   // wave instructions per tensor per tile
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   int qt = item % n_qtiles;
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const int hk = h / group;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in a scalar register
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -103,10 +114,12 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const int q0 = qt * FWD_BR + w * 32;
   const int qi = q0 + l32;
 
-  // A negative scale is folded into Q (exact sign flip) so the exponent factor is >= 0 and the
-  // row maximum of the raw scores gives the maximum of the scaled ones.
+  // The sign of the scale is folded into Q (exact) and its magnitude is kept >= FLT_MIN, so the
+  // exponent factor c is positive: the maximum of the raw scores gives the maximum of the scaled
+  // ones, and masked raw scores of -inf scale to -inf (a zero scale then yields exp2(0) = 1 for
+  // every kept key, the uniform average).
   const bool neg = scale_log2 < 0.f;
-  const float c = neg ? -scale_log2 : scale_log2;
+  const float c = fmaxf(neg ? -scale_log2 : scale_log2, FLT_MIN);
   bf16x8 qf[KSTEPS];
   if (qi < N) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + q_head + (size_t)qi * HD);
@@ -123,27 +136,34 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const int q_end = min(N, qt * FWD_BR + FWD_BR);
   const int n_kt = CAUSAL ? (q_end + FWD_BC - 1) / FWD_BC : (N + FWD_BC - 1) / FWD_BC;
 
-  // Direct-to-LDS staging: a wave instruction covers RPI rows (1 KB); wave w issues blocks
-  // w, w + 4, ... of the tile. Lane i fills row blk*RPI + i / CHUNKS, chunk position i % CHUNKS,
-  // with global chunk position ^ swz(row). Rows past the sequence end re-read row N-1 (finite
-  // data; their scores are masked).
-  constexpr int RPI = 1024 / (HD * 2);
-  constexpr int BLOCKS = FWD_BC / RPI;  // wave instructions per tensor per tile
-  auto issue_tile = [&](int kt, int stage) {
-    const int k0 = kt * FWD_BC;
+  // Direct-to-LDS staging: wave w issues blocks w, w + 4, ... of a tile (RPI rows each). Lane i
+  // fills row blk*RPI + i / CHUNKS at chunk position i % CHUNKS with global chunk
+  // position ^ swz(row). The swizzles repeat within 4*RPI rows, so a lane's byte offset moves by
+  // BLK_BYTES from one of its blocks to the next. The buffer resource of tile kt starts at its
+  // first row and ends at the sequence end, so rows past N load as zeros.
+  constexpr int BLK_BYTES = 4 * RPI * HD * 2;  // byte distance between this wave's blocks
+  const int st_row = w * RPI + lane / CHUNKS;
+  const int k_voff = (st_row * HD + (((lane % CHUNKS) ^ swz_k<HD>(st_row)) * 8)) * 2;
+  const int v_voff = (st_row * HD + (((lane % CHUNKS) ^ swz_v<HD>(st_row)) * 8)) * 2;
+  const bf16* k_head = K + kv_head;
+  const bf16* v_head = V + kv_head;
+  auto issue_k = [&](int kt, int stage) {
+    const int row0 = kt * FWD_BC;
+    const auto rsrc = make_rsrc(k_head + (size_t)row0 * HD, (N - row0) * HD * 2);
 #pragma unroll
-    for (int u = 0; u < BLOCKS / 4; ++u) {
-      const int blk = u * 4 + w;
-      const int row = blk * RPI + lane / CHUNKS;
-      const int pos = lane % CHUNKS;
-      const size_t grow = kv_head + (size_t)min(k0 + row, N - 1) * HD;
-      load_to_lds(K + grow + ((pos ^ swz_k<HD>(row)) * 8), &sm.k[stage][blk * RPI * HD]);
-      load_to_lds(V + grow + ((pos ^ swz_v<HD>(row)) * 8), &sm.v[stage][blk * RPI * HD]);
-    }
+    for (int u = 0; u < BLOCKS / 4; ++u)
+      load_to_lds(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * 4 + w) * RPI * HD]);
+  };
+  auto issue_v = [&](int kt, int stage) {
+    const int row0 = kt * FWD_BC;
+    const auto rsrc = make_rsrc(v_head + (size_t)row0 * HD, (N - row0) * HD * 2);
+#pragma unroll
+    for (int u = 0; u < BLOCKS / 4; ++u)
+      load_to_lds(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * 4 + w) * RPI * HD]);
   };
 
   // K A-operand read (S^T block kb, k-step kk): row 32kb + l32, chunk 2kk + g at position
-  // (2kk + g) ^ swz_k(l32) (32kb is a multiple of CH rows' swizzle period).
+  // (2kk + g) ^ swz_k(l32) (32kb is a multiple of the swizzle period).
   const int k_lane = l32 * HD;
   const int k_t = g ^ swz_k<HD>(l32);
   // Transposed V read: in its 16-lane group, source lane 4e + j points at key row (4g + e) of the
@@ -155,110 +175,139 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const int v_t = v_x ^ swz_v<HD>(v_row);
   const int v_lane = v_row * HD + 4 * (lane & 1);
 
+  // S^T for one tile: block kb rows = keys 32kb + 8(r/4) + 4g + r%4, column = this lane's query.
+  auto scores = [&](const bf16* kbuf, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const bf16* krow = &kbuf[32 * kb * HD + k_lane];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ k_t) * 8), qf[kk], s[kb]);
+    }
+  };
+
   f32x16 oacc[CBLK];
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
   float m_run = -INFINITY;  // reference maximum (log2 units) shared by numerator and normaliser
   float l_run = 0.f;        // this lane's share of the normaliser
 
-  // One K/V tile. MASK selects the path that evaluates the causal / sequence-end masks.
-  auto tile = [&](const int k0, const bf16* kbuf, const bf16* vbuf, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    bool need[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      need[kb] = !MASK || ((k0 + 32 * kb < N) && (!CAUSAL || k0 + 32 * kb <= q0 + 31));
-
-    // S^T block kb: rows = keys k0 + 32kb + 8(r/4) + 4g + r%4, column = this lane's query.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      if (need[kb]) {
-        const bf16* krow = &kbuf[32 * kb * HD + k_lane];
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ k_t) * 8), qf[kk], s[kb]);
-      }
-    }
-
-    float tmax;
-    if constexpr (MASK) {
-      tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = need[kb] && key < N && (!CAUSAL || key <= qi);
-          const float x = ok ? s[kb][r] * c : -INFINITY;  // scaled score, -inf where masked
-          s[kb][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      }
-    } else {
-      float rmax = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) rmax = fmaxf(rmax, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rmax = fmaxf(rmax, s[1][r]);
-      tmax = rmax * c;
-    }
-    tmax = pair_max(tmax);
-    // Tile 0 always holds key 0, which every query row keeps, so m_run is finite after it.
-    const bool raise = tmax > m_run + kLazyRescale;
-    const float m_new = raise ? tmax : m_run;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
-    }
-    m_run = m_new;
-
-    // P^T in the B-operand layout: k-step ks = 2kb + hh takes accumulator slots 8hh .. 8hh+7.
-    bf16x8 pf[4];
+  // Masks raw scores of a boundary tile with -inf (causal diagonal, sequence end).
+  auto apply_mask = [&](int k0, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = MASK ? fast_exp2(s[kb][r] - m_new) : fast_exp2(fmaf(s[kb][r], c, -m_new));
-        l_run += p;
+        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+      }
+    }
+  };
+
+  // Online-softmax step on raw scores s: updates the reference maximum and the normaliser and
+  // returns P^T in the B-operand layout (k-step ks = 2kb + hh takes accumulator slots 8hh..8hh+7).
+  // The output rescale, needed only when the maximum rises, is left to the caller.
+  auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4], float& alpha) {
+    float mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
+    const float rmax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])), fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+    // Tile 0 always holds key 0, which every query row keeps, so m_run is finite after it.
+    const float tmax = pair_max(rmax) * c;
+    const bool raise = tmax > m_run + kLazyRescale;
+    const float m_new = raise ? tmax : m_run;
+    alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float tsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[kb][r], c, -m_new));
+        tsum += p;
         pf[2 * kb + (r >> 3)][r & 7] = to_bf16(p);
       }
     }
+    l_run = fmaf(l_run, alpha, tsum);
+    // The branch condition reads tsum so the exponentials stay ahead of the (rare) rescale branch,
+    // in the basic block that also issues the next tile's score MFMAs.
+    return __builtin_amdgcn_ballot_w64(raise && tsum >= 0.f) != 0;
+  };
 
-    // O^T += V^T P^T. A operand: lane row c = 32cb + l32, keys 32kb + 16hh + {4g..4g+3, 8+4g..8+4g+3}.
+  // O^T += V^T P^T. A operand: lane row c = 32cb + l32, keys 32kb + 16hh + {4g..4g+3, 8+4g..8+4g+3}.
+  auto pv = [&](const bf16* vbuf, const bf16x8 (&pf)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kb = ks >> 1;
       const int hh = ks & 1;
-      if (!need[kb]) continue;
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) {
         const bf16* vp = &vbuf[(32 * kb + 16 * hh) * HD + v_lane + ((4 * cb) ^ v_t) * 8];
-        const bf16x8 va = __builtin_shufflevector(lds_read_tr(vp), lds_read_tr(vp + 8 * HD), 0, 1, 2, 3, 4, 5,
-                                                  6, 7);
+        const bf16x8 va =
+            __builtin_shufflevector(lds_read_tr(vp), lds_read_tr(vp + 8 * HD), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[cb] = mfma32(va, pf[ks], oacc[cb]);
       }
     }
   };
 
-  issue_tile(0, 0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    // This wave's loads of tile kt have landed; after the barrier every wave's have, and every
-    // wave has finished reading the stage that tile kt + 1 overwrites.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 1 < n_kt) issue_tile(kt + 1, (kt + 1) & 1);
+  auto is_boundary = [&](int kt) {
     const int k0 = kt * FWD_BC;
-    const bf16* kbuf = sm.k[kt & 1];
-    const bf16* vbuf = sm.v[kt & 1];
-    const bool boundary = (k0 + FWD_BC > N) || (CAUSAL && k0 + FWD_BC - 1 > q0);
-    if (boundary)
-      tile(k0, kbuf, vbuf, std::integral_constant<bool, true>{});
-    else
-      tile(k0, kbuf, vbuf, std::integral_constant<bool, false>{});
+    return (k0 + FWD_BC > N) || (CAUSAL && k0 + FWD_BC - 1 > q0);
+  };
+
+  // Prologue: K0, V0 and K1 in flight, then S^T of tile 0.
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (n_kt > 1) issue_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 s_cur[2];
+  scores(sm.k[0], s_cur);
+  __syncthreads();  // every wave has read K0 before its stage is reused for K2
+
+  // One pipelined step. Entering it: sc = S^T of tile kt, K_{kt+1} and V_kt in LDS. It issues the
+  // loads of V_{kt+1} and K_{kt+2}, the score MFMAs of tile kt+1 (into sn) together with the
+  // softmax of tile kt, then O += V_kt P_kt, and ends at a barrier.
+  auto step = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    issue_v(kt + 1, (kt + 1) & 1);
+    if (kt + 2 < n_kt) issue_k(kt + 2, kt & 1);
+    if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
+    bf16x8 pf[4];
+    float alpha;
+    scores(sm.k[(kt + 1) & 1], sn);                // matrix cores: tile kt + 1
+    const bool rescale = softmax(sc, pf, alpha);  // vector ALUs: tile kt
+    if (rescale) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+    }
+    pv(sm.v[kt & 1], pf);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of V_{kt+1}, K_{kt+2} have landed
+    __syncthreads();                // ... and every wave's; stages read in this step are free
+  };
+  // The last tile: softmax and O += V P only.
+  auto last = [&](int kt, f32x16 (&sc)[2]) {
+    if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
+    bf16x8 pf[4];
+    float alpha;
+    if (softmax(sc, pf, alpha)) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+    }
+    pv(sm.v[kt & 1], pf);
+  };
+  // Two steps per trip so the two score buffers trade roles instead of being copied.
+  f32x16 s_alt[2];
+  int kt = 0;
+  for (; kt + 2 < n_kt; kt += 2) {
+    step(kt, s_cur, s_alt);
+    step(kt + 1, s_alt, s_cur);
+  }
+  if (kt + 1 < n_kt) {
+    step(kt, s_cur, s_alt);
+    last(kt + 1, s_alt);
+  } else {
+    last(kt, s_cur);
   }
 
   l_run += __shfl_xor(l_run, 32, 64);
