@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libroofattn.so")
+# ROOFATTN_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("ROOFATTN_LIB", os.path.join(_HERE, "libroofattn.so"))
 
 ATTN_F32, ATTN_BF16 = 0, 1
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}

@@ -29,28 +29,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: ROCm is required to build libroofattn.so")
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(src: str, extra=(), objdir=OBJ) -> str:
+    out = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB) -> str:
+    """Compiles every source and links the library; extra_flags/lib_path build a tuning variant."""
+    objdir = OBJ if lib_path == LIB else lib_path + ".objs"
+    os.makedirs(objdir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, tuple(extra_flags), objdir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":

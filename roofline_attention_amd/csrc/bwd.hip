@@ -11,24 +11,41 @@
 //
 // Kernels, per (batch, head):
 //   bwd_pre : D_i = sum_t dO[i,t] * O[i,t]   (equals sum_j P_ij dP_ij)
-//   bwd_dkdv: workgroup = 128 keys (4 waves x 32); loops over 32-query tiles:
+//   bwd_dkdv: workgroup = 128 keys (4 waves x 32, K and V of its keys in registers); streams
+//             64-query tiles of Q, dO, LSE and D through double-buffered LDS:
 //             S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e), dV += P^T dO, dP = dO V^T,
 //             dS = P (dP - D), dK += dS^T Q; stores dK * scale and dV.
-//   bwd_dq  : workgroup = 128 queries (4 waves x 32); loops over 64-key tiles:
-//             S^T = K Q^T, P^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
-//             stores dQ * scale.
+//   bwd_dq  : workgroup = 128 queries (4 waves x 32, Q and dO of its rows in registers); streams
+//             64-key tiles of K and V: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T = P^T (dP^T - D),
+//             dQ^T += K^T dS^T; stores dQ * scale.
 // MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to bf16 (nearest
-// even) as MFMA operands. Operands whose contraction index is the row index of a stored tile are
-// read from a transposed LDS copy made when the tile is staged.
+// even) as MFMA operands. The probabilities and dS come out of the score accumulators already in
+// the A/B-operand layout their next product needs. Operands that contract over the rows of a
+// staged tile (dO and Q for dV and dK, K for dQ) come from ds_read_b64_tr_b16 on the row-major
+// tile, so nothing is transposed in memory. Tiles reach LDS by direct buffer loads whose range
+// check zero-fills rows past the sequence end; zero Q/dO rows and zero K/V rows contribute
+// nothing to any stored gradient, so only the causal diagonal needs a mask.
 #include <math.h>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tile.hpp"
 
 namespace ra {
 namespace {
 
 constexpr int BWD_THREADS = 256;
+// Waves per SIMD the register budget is sized for. The key-major kernel holds K, V operands and
+// fp32 dK, dV accumulators (about 330 registers): one wave per SIMD keeps the accumulators in
+// AGPRs without spilling, which measured faster than two spilling waves.
+#ifndef RA_DKDV_WAVES_PER_SIMD
+#define RA_DKDV_WAVES_PER_SIMD 1
+#endif
+#ifndef RA_DQ_WAVES_PER_SIMD
+#define RA_DQ_WAVES_PER_SIMD 2
+#endif
+constexpr int BWD_BQ = 64;   // queries per staged tile in the key-major kernel
+constexpr int BWD_BK = 64;   // keys per staged tile in the query-major kernel
 
 // ------------------------------------------------------------------------- preprocess ----
 
@@ -55,66 +72,60 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_pre_kernel(const bf16* __rest
   if (row < rows && c == 0) D[row] = x;
 }
 
-// Stages a [32 rows x HD] bf16 tile into a row-major copy (stride HD + 8) and, optionally, a
-// transposed copy (stride 32 + 4 per head-dimension row). Rows at or beyond n_rows are zero.
-template <int HD, bool TRANSPOSED>
-__device__ __forceinline__ void stage_rows32(const bf16* __restrict__ src, int row0, int n_rows,
-                                             bf16* rm, bf16* tr, int tid) {
-  constexpr int CH = HD / 8;
-  constexpr int R = HD / 64;  // rows per thread (32 * CH / 256)
-  const int cc = tid % CH;
-  const int rg = tid / CH;
-  bf16x8 x[R];
-#pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int row = rg * R + u;
-    x[u] = row0 + row < n_rows ? *reinterpret_cast<const bf16x8*>(src + (size_t)(row0 + row) * HD + cc * 8)
-                               : bf16x8{};
-    *reinterpret_cast<bf16x8*>(rm + row * (HD + 8) + cc * 8) = x[u];
+// Per-lane constants of the transposed read over a [rows][HD] tile with swizzle SWZ: in its
+// 16-lane group, source lane 4e + j points at row (4g + e) of an 8-row-aligned block and element
+// column 16 * ((lane / 16) % 2) + 4j of a 32-column block. The swizzle of that row depends on the
+// block's row base only through its bit 3 (the second half of a 16-row k-step), so two lane
+// constants cover both halves. Returns the element offset for (row base rb, column block cb).
+template <int HD, int (*SWZ)(int)>
+struct TrLane {
+  int row_off;  // (4g + e) * HD + 4 * (j & 1)
+  int t0, t8;   // chunk XOR constants for row bases = 0 and = 8 (mod 16)
+  __device__ __forceinline__ TrLane(int lane) {
+    const int g = lane >> 5;
+    const int e = (lane & 15) >> 2;
+    const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    row_off = (4 * g + e) * HD + 4 * (lane & 1);
+    t0 = x ^ SWZ(4 * g + e);
+    t8 = x ^ SWZ(8 + 4 * g + e);
   }
-  if constexpr (TRANSPOSED) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16* dst = tr + (cc * 8 + e) * (32 + 4) + rg * R;
-      if constexpr (R == 2) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<bf16x2*>(dst) = bf16x2{x[0][e], x[1][e]};
-      } else {
-        dst[0] = x[0][e];
-      }
-    }
+  // element offset of this lane's 4 x bf16 for rows rb + (4g + e), 32-column block cb
+  __device__ __forceinline__ int at(int rb, int cb) const {
+    return rb * HD + row_off + ((4 * cb) ^ ((rb & 8) ? t8 : t0)) * 8;
   }
+};
+
+template <int HD>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, const TrLane<HD, swz_both<HD>>& tl, int rb, int cb) {
+  return __builtin_shufflevector(lds_read_tr(tile + tl.at(rb, cb)), lds_read_tr(tile + tl.at(rb + 8, cb)), 0, 1, 2,
+                                 3, 4, 5, 6, 7);
 }
 
 // ------------------------------------------------------------------------------ dK dV ----
 
 template <int HD>
 struct DkdvSmem {
-  bf16 q[32 * (HD + 8)];
-  bf16 qt[HD * 36];
-  bf16 dO[32 * (HD + 8)];
-  bf16 dOt[HD * 36];
-  float lse2[32];
-  float Dv[32];
+  bf16 q[2][BWD_BQ * HD];
+  bf16 dO[2][BWD_BQ * HD];
+  float lse[2][BWD_BQ];
+  float dd[2][BWD_BQ];
 };
 
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dK, float* __restrict__ dV, int H, int N, int n_ktiles, float scale,
-    float scale_log2) {
-  __shared__ DkdvSmem<HD> sm;
+    float* __restrict__ dK, float* __restrict__ dV, int N, int n_ktiles, float scale, float scale_log2) {
+  extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+  DkdvSmem<HD>& sm = *reinterpret_cast<DkdvSmem<HD>*>(dyn_smem);
   constexpr int KSTEPS = HD / 16;
   constexpr int CBLK = HD / 32;
-  constexpr int QS = HD + 8;
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
-  int kt = item % n_ktiles;
+  const int kt = item % n_ktiles;  // causal: low key tiles see the most query tiles and go first
   const int bh = item / n_ktiles;
-  if (CAUSAL) kt = n_ktiles - 1 - kt;  // (causal) low key tiles carry the most query tiles
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -122,7 +133,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dkdv_kernel(
   const size_t head = (size_t)bh * N * HD;
   const size_t rowbase = (size_t)bh * N;
   const int kw0 = kt * 128 + w * 32;  // this wave's first key
-  const int key = kw0 + l32;          // B-operand column owned by this lane
+  const int key = kw0 + l32;          // the key column this lane holds in S and dP
 
   bf16x8 kf[KSTEPS], vf[KSTEPS];
   if (key < N) {
@@ -142,56 +153,71 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dkdv_kernel(
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) dk[cb] = dv[cb] = f32x16{};
 
-  const int n_qt = (N + 31) / 32;
-  const int first_qt = CAUSAL ? (kt * 128) / 32 : 0;
-  for (int qt = first_qt; qt < n_qt; ++qt) {
-    const int i0 = qt * 32;
-    __syncthreads();
-    stage_rows32<HD, true>(Q + head, i0, N, sm.q, sm.qt, tid);
-    stage_rows32<HD, true>(dO + head, i0, N, sm.dO, sm.dOt, tid);
-    if (tid < 32) {
-      const int i = i0 + tid;
-      sm.lse2[tid] = i < N ? LSE[rowbase + i] * kLog2e : INFINITY;
-      sm.Dv[tid] = i < N ? Dg[rowbase + i] : 0.f;
-    }
-    __syncthreads();
-    if (CAUSAL && i0 + 31 < kw0) continue;  // every query of the tile precedes every key of the wave
-    if (kw0 >= N) continue;
+  const TrLane<HD, swz_both<HD>> tl(lane);
+  // Row-operand reads (A = Q or dO rows of a 32-query block): row qb*32 + l32, chunk 2kk + g.
+  const int row_t = g ^ swz_both<HD>(l32);  // swz_both repeats every 16 rows
+  const int row_off = l32 * HD;
+  const bf16* Qh = Q + head;
+  const bf16* dOh = dO + head;
+  const float* LSEh = LSE + rowbase;
+  const float* Dh = Dg + rowbase;
 
-    // S and dP: lane column = key, rows = queries i0 + 8(r/4) + 4g + r%4.
-    f32x16 s = f32x16{}, dp = f32x16{};
-    const bf16* qrow = &sm.q[l32 * QS + 8 * g];
-    const bf16* drow = &sm.dO[l32 * QS + 8 * g];
+  auto stage = [&](int qt, int s) {
+    const int r0 = qt * BWD_BQ;
+    stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(Qh, r0, N, sm.q[s], w, lane);
+    stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(dOh, r0, N, sm.dO[s], w, lane);
+    if (w == 0) load_to_lds<4>(make_rsrc(LSEh + r0, (N - r0) * 4), lane * 4, sm.lse[s]);
+    if (w == 1) load_to_lds<4>(make_rsrc(Dh + r0, (N - r0) * 4), lane * 4, sm.dd[s]);
+  };
+
+  const int n_qt = (N + BWD_BQ - 1) / BWD_BQ;
+  const int first_qt = CAUSAL ? (kt * 128) / BWD_BQ : 0;
+  stage(first_qt, first_qt & 1);
+  for (int qt = first_qt; qt < n_qt; ++qt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // tile qt is in LDS everywhere; the other stage is free
+    if (qt + 1 < n_qt) stage(qt + 1, (qt + 1) & 1);
+    const int s = qt & 1;
+    const bf16* qtile = sm.q[s];
+    const bf16* dtile = sm.dO[s];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      s = mfma32(*reinterpret_cast<const bf16x8*>(qrow + 16 * kk), kf[kk], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vf[kk], dp);
-    }
-    bf16x8 pb[2], dsb[2];
+    for (int qb = 0; qb < BWD_BQ / 32; ++qb) {
+      const int i0 = qt * BWD_BQ + qb * 32;
+      if (CAUSAL && i0 + 31 < kw0) continue;  // every query of the block precedes every key of the wave
+      // S and dP: lane column = key, rows = queries i0 + 8(r/4) + 4g + r%4.
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      const bf16* qrow = qtile + qb * 32 * HD + row_off;
+      const bf16* drow = dtile + qb * 32 * HD + row_off;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int il = 8 * (r >> 2) + 4 * g + (r & 3);
-      const int i = i0 + il;
-      const bool ok = key < N && (!CAUSAL || key <= i);  // rows i >= N have lse2 = +inf -> P = 0
-      const float p = ok ? fast_exp2(s[r] * scale_log2 - sm.lse2[il]) : 0.f;
-      const float ds = p * (dp[r] - sm.Dv[il]);
-      pb[r >> 3][r & 7] = to_bf16(p);
-      dsb[r >> 3][r & 7] = to_bf16(ds);
-    }
-    // dV += P^T dO and dK += dS^T Q. A operand: lane row = key, k-step hh covers queries
-    // 16hh + {4g..4g+3, 8+4g..8+4g+3}; B operand: column c = 32cb + l32 from the transposed tile.
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const int off = ((2 * kk) ^ row_t) * 8;
+        sacc = mfma32(*reinterpret_cast<const bf16x8*>(qrow + off), kf[kk], sacc);
+        dpacc = mfma32(*reinterpret_cast<const bf16x8*>(drow + off), vf[kk], dpacc);
+      }
+      const bool diag = CAUSAL && i0 < kw0 + 32;  // some key of the wave follows some query of the block
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[s][qb * 32 + 8 * rg + 4 * g]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[s][qb * 32 + 8 * rg + 4 * g]);
 #pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) {
-        const bf16* dt = &sm.dOt[(32 * cb + l32) * 36 + 16 * hh + 4 * g];
-        const bf16* qq = &sm.qt[(32 * cb + l32) * 36 + 16 * hh + 4 * g];
-        const bf16x8 bdo = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(dt),
-                                                   *reinterpret_cast<const bf16x4*>(dt + 8), 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 bq = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(qq),
-                                                  *reinterpret_cast<const bf16x4*>(qq + 8), 0, 1, 2, 3, 4, 5, 6, 7);
-        dv[cb] = mfma32(pb[hh], bdo, dv[cb]);
-        dk[cb] = mfma32(dsb[hh], bq, dk[cb]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e] * kLog2e));
+          if (diag && key > i0 + 8 * rg + 4 * g + e) p = 0.f;
+          pb[r >> 3][r & 7] = to_bf16(p);
+          dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - d4[e]));
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane row = key, k-step hh covers queries
+      // 16hh + {4g..4g+3, 8+4g..8+4g+3}); B = dO / Q columns 32cb + l32 by transposed read.
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) {
+          dv[cb] = mfma32(pb[hh], tr_operand<HD>(dtile, tl, qb * 32 + 16 * hh, cb), dv[cb]);
+          dk[cb] = mfma32(dsb[hh], tr_operand<HD>(qtile, tl, qb * 32 + 16 * hh, cb), dk[cb]);
+        }
       }
     }
   }
@@ -214,29 +240,25 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dkdv_kernel(
 
 template <int HD>
 struct DqSmem {
-  bf16 k[64 * (HD + 8)];
-  bf16 kt[HD * 68];
-  bf16 v[64 * (HD + 8)];
+  bf16 k[2][BWD_BK * HD];
+  bf16 v[2][BWD_BK * HD];
 };
 
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dQ, int H, int N, int n_qtiles, float scale, float scale_log2) {
+    float* __restrict__ dQ, int N, int n_qtiles, float scale, float scale_log2) {
   __shared__ DqSmem<HD> sm;
   constexpr int KSTEPS = HD / 16;
   constexpr int CBLK = HD / 32;
-  constexpr int KS = HD + 8;
-  constexpr int CH = HD / 8;
-  constexpr int LOADS = 64 * CH / BWD_THREADS;  // 16-byte chunks per thread per tile (K or V)
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   int qt = item % n_qtiles;
   const int bh = item / n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // heaviest query tiles first
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -247,7 +269,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dq_kernel(
   const int qi = q0 + l32;
 
   bf16x8 qf[KSTEPS], df[KSTEPS];
-  float lse2 = INFINITY, Dq = 0.f;
+  float lse2 = 0.f, Dq = 0.f;  // rows past N: Q = dO = 0 gives dS = 0
   if (qi < N) {
     const bf16x8* qs = reinterpret_cast<const bf16x8*>(Q + head + (size_t)qi * HD);
     const bf16x8* ds = reinterpret_cast<const bf16x8*>(dO + head + (size_t)qi * HD);
@@ -267,80 +289,53 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void bwd_dq_kernel(
 #pragma unroll
   for (int cb = 0; cb < CBLK; ++cb) acc[cb] = f32x16{};
 
+  const TrLane<HD, swz_both<HD>> tl(lane);
+  const int krow_t = g ^ swz_both<HD>(l32);
+  const int vrow_t = g ^ swz_rows<HD>(l32);
+  const int row_off = l32 * HD;
+  const bf16* Kh = K + head;
+  const bf16* Vh = V + head;
+
+  auto stage = [&](int t, int s) {
+    stage_tile<HD, BWD_BK, 4, swz_both<HD>>(Kh, t * BWD_BK, N, sm.k[s], w, lane);
+    stage_tile<HD, BWD_BK, 4, swz_rows<HD>>(Vh, t * BWD_BK, N, sm.v[s], w, lane);
+  };
+
   const int q_end = min(N, qt * 128 + 128);
-  const int n_kt = CAUSAL ? (q_end + 63) / 64 : (N + 63) / 64;
-  const int vc = tid % CH;
-  const int vg = tid / CH;  // LOADS consecutive keys per thread for the transposed K copy
+  const int n_kt = CAUSAL ? (q_end + BWD_BK - 1) / BWD_BK : (N + BWD_BK - 1) / BWD_BK;
+  stage(0, 0);
   for (int t = 0; t < n_kt; ++t) {
-    const int k0 = t * 64;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    {
-      bf16x8 kx[LOADS];
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int c = tid + BWD_THREADS * u;
-        const int row = c / CH;
-        const int col = c % CH;
-        const bool in = k0 + row < N;
-        const bf16x8 kv = in ? *reinterpret_cast<const bf16x8*>(K + head + (size_t)(k0 + row) * HD + col * 8) : bf16x8{};
-        const bf16x8 vv = in ? *reinterpret_cast<const bf16x8*>(V + head + (size_t)(k0 + row) * HD + col * 8) : bf16x8{};
-        *reinterpret_cast<bf16x8*>(&sm.k[row * KS + col * 8]) = kv;
-        *reinterpret_cast<bf16x8*>(&sm.v[row * KS + col * 8]) = vv;
-        const int krow = vg * LOADS + u;
-        kx[u] = k0 + krow < N ? *reinterpret_cast<const bf16x8*>(K + head + (size_t)(k0 + krow) * HD + vc * 8)
-                              : bf16x8{};
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16* dst = &sm.kt[(vc * 8 + e) * 68 + vg * LOADS];
-        if constexpr (LOADS == 4) {
-          *reinterpret_cast<bf16x4*>(dst) = bf16x4{kx[0][e], kx[1][e], kx[2][e], kx[3][e]};
-        } else {
-          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          *reinterpret_cast<bf16x2*>(dst) = bf16x2{kx[0][e], kx[1][e]};
-        }
-      }
-    }
-    __syncthreads();
-
-    bool need[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) need[kb] = (k0 + 32 * kb < N) && (!CAUSAL || k0 + 32 * kb <= q0 + 31);
-
+    if (t + 1 < n_kt) stage(t + 1, (t + 1) & 1);
+    const int s = t & 1;
+    const int k0 = t * BWD_BK;
+    const bool diag = CAUSAL && k0 + BWD_BK - 1 > q0;
     bf16x8 dsb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-      if (need[kb]) {
-        const bf16* krow = &sm.k[(32 * kb + l32) * KS + 8 * g];
-        const bf16* vrow = &sm.v[(32 * kb + l32) * KS + 8 * g];
+      // S^T and dP^T: lane column = query, rows = keys k0 + 32kb + 8(r/4) + 4g + r%4.
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      const bf16* krow = sm.k[s] + kb * 32 * HD + row_off;
+      const bf16* vrow = sm.v[s] + kb * 32 * HD + row_off;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          s = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * kk), qf[kk], s);
-          dp = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * kk), df[kk], dp);
-        }
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ krow_t) * 8), qf[kk], sacc);
+        dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + ((2 * kk) ^ vrow_t) * 8), df[kk], dpacc);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kr = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = need[kb] && kr < N && (!CAUSAL || kr <= qi);
-        const float p = ok ? fast_exp2(s[r] * scale_log2 - lse2) : 0.f;
-        dsb[2 * kb + (r >> 3)][r & 7] = to_bf16(p * (dp[r] - Dq));
+        float p = fast_exp2(fmaf(sacc[r], scale_log2, -lse2));
+        if (diag && k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p = 0.f;
+        dsb[2 * kb + (r >> 3)][r & 7] = to_bf16(p * (dpacc[r] - Dq));
       }
     }
-    // dQ^T += K^T dS^T: A operand = K^T row c = 32cb + l32, keys 32kb + 16hh + {4g.., 8+4g..}.
+    // dQ^T += K^T dS^T: A = K^T (rows c = 32cb + l32 by transposed read of the key tile).
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int kb = ks >> 1;
-      const int hh = ks & 1;
-      if (!need[kb]) continue;
 #pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) {
-        const bf16* kr = &sm.kt[(32 * cb + l32) * 68 + 32 * kb + 16 * hh + 4 * g];
-        const bf16x8 a = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(kr),
-                                                 *reinterpret_cast<const bf16x4*>(kr + 8), 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[cb] = mfma32(a, dsb[ks], acc[cb]);
-      }
+      for (int cb = 0; cb < CBLK; ++cb)
+        acc[cb] = mfma32(tr_operand<HD>(sm.k[s], tl, 16 * ks, cb), dsb[ks], acc[cb]);
     }
   }
 
@@ -380,17 +375,25 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   if (err != hipSuccess) return err;
   const int n_t = (N + 127) / 128;
   const unsigned total = (unsigned)((long long)n_t * H * B);
+  const size_t dkdv_smem = sizeof(DkdvSmem<HD>);
+  static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
+  if (!attr_set) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<HD, CAUSAL>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dkdv_smem);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
   {
     TimedScope ts(dkdv_name, stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, stream, Q, K, V, dO,
-                       lse, D, dk, dv, H, N, n_t, scale, scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), dkdv_smem, stream, Q, K, V,
+                       dO, lse, D, dk, dv, N, n_t, scale, scale * kLog2e);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   {
     TimedScope ts(dq_name, stream);
     hipLaunchKernelGGL((bwd_dq_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, stream, Q, K, V, dO, lse,
-                       D, dq, H, N, n_t, scale, scale * kLog2e);
+                       D, dq, N, n_t, scale, scale * kLog2e);
   }
   return hipGetLastError();
 }
