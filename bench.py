@@ -47,6 +47,43 @@ def kernel_stats(lib, before=None):
     return {k: {"launches": n, "avg_ms": ms / n if n else None, "total_ms": ms} for k, (n, ms) in rec.items()}
 
 
+def calibration_copy(torch, nbytes=1 << 30):
+    """A plain elementwise copy kernel of known size (dst = -src over 1 GiB of float32: 1 GiB read,
+    1 GiB written, larger than the last-level cache), run once before timing. Its FETCH_SIZE /
+    WRITE_SIZE counters in a profiler run of this same command calibrate the byte counters of the
+    attention kernels."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def kernel_sources_digest(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "roofline_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or ent.get("sources_sha256") != kernel_sources_digest(ent.get("sources", [])):
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
 def time_region(torch, lib, fn, steps):
     """Runs fn() `steps` times between synchronisations; returns (wall seconds, kernel stats)."""
     lib.timing_reset()
@@ -110,6 +147,7 @@ def main():
     from roofline_attention_amd import ledger as L
 
     torch.cuda.set_device(0)
+    calibration_copy(torch)
     w = I.WORKLOADS["fwdbwd_4k_causal"]
     log(f"[bench] inputs {w}")
     t = {k: x.cuda() for k, x in I.make_prefill(w, with_dout=True).items()}
@@ -165,7 +203,7 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": amount / avg_s / 1e9, "peak": L.PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["avg_ms"] = stats[dom]["avg_ms"]
     roof["algorithmic_per_launch"] = amount
 
