@@ -72,6 +72,12 @@ def decode_intensity(g: int, s: int) -> float:
     return 2.0 * g / s
 
 
+def round_trip_bytes(M: int, N: int, s: int) -> float:
+    """Bytes a fused kernel removes by not writing and re-reading an M x N intermediate
+    ("M4.2 - GPU Execution Model for Transformer Kernels", section 0x08 fusion ledger)."""
+    return 2.0 * M * N * s
+
+
 def moa_naive_fwd_bytes(B: int, N: int, D: int, s: int = 8):
     """Bytes of the MoA paper's naive forward (reads Q, K, V; writes the n x n matrix A and Out)."""
     reads = 3.0 * B * N * D * s
