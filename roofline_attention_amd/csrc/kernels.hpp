@@ -32,8 +32,8 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           hipStream_t stream);
 
 // Decode split size (keys per workgroup) and workspace layout: per (b, h, split) a record of
-// d + 2 floats {m, l, o[0..d)} (m in log2 units of the scaled score).
-constexpr int kDecodeSplit = 256;
+// d + 4 floats {m, l, -, -, o[0..d)} (m in log2 units of the scaled score, o not yet divided by l).
+constexpr int kDecodeSplit = 1024;
 size_t decode_workspace_bytes(int B, int H, int N_cap, int d);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* lse,
                          const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d,

@@ -32,6 +32,10 @@ __device__ __forceinline__ int swz_both(int r) {
   return (4 * (r & 3) + ((r >> 2) & 3)) & (HD / 8 - 1);
 }
 
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 // Raw buffer resource over `bytes` bytes from `base`; loads at or beyond `bytes` return zero
 // without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
@@ -53,6 +57,33 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rsrc, int vof
 // of a 4-row block; lane i of the group receives the 4 elements of column i of that block.
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
+}
+
+// The same read issued as inline assembly. The compiler's wait insertion treats the builtin form
+// as aliasing every direct-to-LDS load still in flight and waits for all of them (vmcnt(0)); a
+// kernel that keeps the next tile's loads in flight across its reads of the current tile uses this
+// form instead and orders it itself: the result may be used only after lds_wait(), which waits
+// for all of this wave's LDS reads and ties the results so that no use is scheduled earlier.
+__device__ __forceinline__ bf16x4 lds_read_tr_async(const bf16* p) {
+  bf16x4 r;
+  const unsigned addr = (unsigned)(uintptr_t)((const bf16 __attribute__((address_space(3)))*)p);
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 tr_pair_async(const bf16* p0, const bf16* p1) {
+  return __builtin_shufflevector(lds_read_tr_async(p0), lds_read_tr_async(p1), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_all(bf16x8 (&a)[N]) {
+  static_assert(N == 4 || N == 8, "operand batch");
+  if constexpr (N == 4) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]));
+  }
 }
 
 // Stages ROWS x HD bf16 rows [row0, row0 + ROWS) of a row-major [n_rows, HD] matrix into an LDS

@@ -89,7 +89,7 @@ def test_fwd_rejects_null_misaligned_and_overlapping(lib):
 def test_decode_validation(lib):
     p = [addr(i) for i in range(7)]
     ws_need = lib.attn_decode_workspace_size(64, 32, 8192, 128)
-    assert ws_need == 64 * 32 * 32 * (128 + 4) * 4
+    assert ws_need == 64 * 32 * 8 * (128 + 4) * 4  # 1024-key splits
 
     def call(B=64, H=32, H_kv=8, N_cap=8192, d=128, dtype=BF16, ws=p[6], ws_bytes=ws_need, kv=p[5]):
         return lib.attn_decode(p[0], p[1], p[2], p[3], p[4], kv, B, H, H_kv, N_cap, d, 0, 0.088, dtype, ws,
