@@ -84,7 +84,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  *   `causal` is accepted for signature symmetry and ignored: the single query follows every key.
  *   workspace: device buffer of at least attn_decode_workspace_size(B, H, N_cap, d) bytes,
  *   16-byte aligned, contents need no initialisation; it is scratch owned by the caller.
- * dtype must be ATTN_BF16.
+ * dtype must be ATTN_BF16; H / H_kv must be 1, 2, 4 or 8; B * H_kv must be below 2^24.
  */
 size_t attn_decode_workspace_size(int B, int H, int N_cap, int d);
 attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

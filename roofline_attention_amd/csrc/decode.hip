@@ -9,11 +9,10 @@
 // Model for Transformer Kernels", section 0x08: split-K trades parallelism for an extra
 // reduction pass).
 //
-// Split kernel, one 4-wave workgroup per (1024-key split, KV head, sequence); within a wave,
-//   lane = (key slot ks, 16-byte chunk dc of the head dimension). One load instruction covers
-//   KPI consecutive cache rows (contiguous bytes), the partial dot products are joined across the
-//   chunk lanes with DPP, and the softmax is kept online over sub-chunks of ITERS * KPI keys whose
-//   loads are issued one sub-chunk ahead. The partial record of each query head is
+// Split kernel, one 4-wave workgroup per (sequence, KV head, 1024-key split), launched split-major
+//   so the 8 XCDs share every split evenly; each wave streams 256 keys in 32-key tiles held in
+//   registers (two tiles in flight), S^T and O^T on 16x16x32 bf16 MFMAs, and the waves' partial
+//   (max, sum, output) triples are merged in LDS. The record of each query head and split is
 //   {m, l, -, -, o[d]} with m in log2 units of the scaled score and o not yet divided by l.
 // Combine kernel, one wave per (query head, sequence): M = max m_s, L = sum 2^(m_s - M) l_s,
 //   O = sum 2^(m_s - M) o_s / L, LSE = ln 2 * (M + log2 L).
@@ -29,8 +28,7 @@ namespace {
 
 constexpr int DEC_WAVES = 4;                             // waves per workgroup
 constexpr int DEC_WAVE_KEYS = kDecodeSplit / DEC_WAVES;  // keys per wave (256)
-constexpr int DEC_TILE = 32;                             // keys per LDS stage
-constexpr int DEC_STAGES = 2;
+constexpr int DEC_TILE = 32;                             // keys per tile
 
 __device__ __forceinline__ int clamp_len(const int32_t* kv_len, int b, int N_cap) {
   const int len = kv_len[b];
@@ -41,15 +39,11 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Per-wave LDS: DEC_STAGES stages of a DEC_TILE-key K tile and V tile, unpadded rows with the
-// 16-byte chunk c of row r at position c ^ swz(r). K is read as MFMA A-operand rows (16 rows, one
-// chunk per 16-lane group: swz_k = r mod CH); V by transposed reads (8 rows x 2 chunks per 32
-// lanes: swz_v = 2r mod CH).
-template <int HD>
-struct DecodeWaveSmem {
-  bf16 k[DEC_STAGES][DEC_TILE * HD];
-  bf16 v[DEC_STAGES][DEC_TILE * HD];
-};
+// K/V bytes are read exactly once: loads carry the non-temporal cache policy (gfx950 cache-policy
+// bit 1, "nt"), which keeps the stream from displacing other lines; measured 10% faster here.
+__device__ __forceinline__ bf16x8 buffer_load16_nt(__amdgpu_buffer_rsrc_t rsrc, int voffset) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, 2));
+}
 
 template <int HD, int G>
 struct DecodeMerge {
@@ -58,39 +52,40 @@ struct DecodeMerge {
   float o[DEC_WAVES][G][HD];
 };
 
-template <int HD>
-constexpr size_t decode_smem_bytes(int G) {
-  const size_t stages = sizeof(DecodeWaveSmem<HD>) * DEC_WAVES;
-  const size_t merge = (size_t)DEC_WAVES * G * (HD + 2) * sizeof(float);
-  return stages > merge ? stages : merge;
-}
-
-
 // One workgroup = 4 waves over kDecodeSplit consecutive keys of one (sequence, KV head); wave w
 // takes keys [256w, 256w + 256) of the split and works independently of the other waves until
-// the final merge. Per 32-key tile (HBM -> LDS by buffer_load ... lds, two stages in flight):
-//   S^T = K Q^T on 16x16x32 MFMAs (A = 16 keys x 32 d from LDS, B = the g query heads of the KV
-//   head as columns, padded with zero columns to 16), online softmax per head on the few lanes
-//   that hold real heads, O^T += V^T P^T on 16x16x32 MFMAs with V^T from transposed LDS reads.
-// The matrix cores do the dot products that would otherwise cost several vector ops per byte;
-// the vector ALUs only run the softmax of 32 keys x g heads per tile.
+// the final merge. Decode moves bytes, so the kernel is organised around keeping enough of them
+// in flight: by Little's law the HBM rate needs roughly rate x latency bytes outstanding, more
+// than the LDS can buffer, so each wave stages its 32-key K/V tiles in registers, two tiles in
+// flight (the register file is several times larger than the LDS). Per tile:
+//   S^T = K Q^T on 16x16x32 MFMAs, the K rows used directly from registers as the A operand
+//   (16 keys x 32 d), Q^T as the B operand (the g query heads as columns, zero-padded to 16);
+//   online softmax per head on the few lanes that hold real heads;
+//   V written to the wave's LDS tile and read back transposed as the A operand of
+//   O^T += V^T P^T (16x16x32 MFMAs).
+// Register loads of tiles past the wave's last key return zeros (buffer range check).
 template <int HD, int G>
-__global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
+__global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
     const bf16* __restrict__ Qd, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int32_t* __restrict__ kv_len, float* __restrict__ ws, int H, int H_kv, int N_cap,
     int n_split, float scale_log2) {
   constexpr int CH = HD / 8;        // 16-byte chunks per row
   constexpr int KSTEPS = HD / 32;   // 16x16x32 k-steps over d
   constexpr int CB = HD / 16;       // 16-row blocks of O^T
-  constexpr int RPI = 1024 / (HD * 2);       // rows per direct-load instruction
-  constexpr int LOADS = DEC_TILE / RPI;      // instructions per tensor per tile
+  constexpr int VROWS = 64 / CH;    // V rows per wave load instruction
+  constexpr int VLOADS = DEC_TILE / VROWS;
   constexpr int REC = HD + 4;
   static_assert(G <= 16, "query heads per KV head");
-  extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+  __shared__ bf16 vtile[DEC_WAVES][DEC_TILE * HD];
+  __shared__ DecodeMerge<HD, G> mg;
 
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
+  // Grid (B * H_kv, n_split), x fastest: workgroups reach the 8 XCDs round-robin in launch order,
+  // so consecutive ids walk the (sequence, KV head) pairs of one split and every XCD gets an even
+  // share of each split. (With the split index fastest, split s would always land on XCD s mod 8
+  // and short sequences would load only the first few XCDs.)
+  const int split = blockIdx.y;
+  const int hk = blockIdx.x % H_kv;
+  const int b = blockIdx.x / H_kv;
   const int len = clamp_len(kv_len, b, N_cap);
   const int k_begin = split * kDecodeSplit;
   if (k_begin >= len) return;  // uniform over the workgroup, before any barrier
@@ -103,7 +98,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
   const int kw_end = min(len, kw_begin + DEC_WAVE_KEYS);
   const int n_keys = max(kw_end - kw_begin, 0);
   const int n_tiles = (n_keys + DEC_TILE - 1) / DEC_TILE;
-  DecodeWaveSmem<HD>& sm = reinterpret_cast<DecodeWaveSmem<HD>*>(dyn_smem)[w];
+  bf16* vt = vtile[w];
 
   // Q^T as the B operand: column col = head hk*G + col, k-group q4 holds d = 32kk + 8q4 .. +7.
   bf16x8 qf[KSTEPS];
@@ -114,28 +109,34 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
   }
 
   const size_t head = ((size_t)b * H_kv + hk) * (size_t)N_cap * HD;
-  // Resources over this wave's keys only: rows at or past kw_end load as zeros.
   const auto krs = make_rsrc(Kc + head + (size_t)kw_begin * HD, n_keys * HD * 2);
   const auto vrs = make_rsrc(Vc + head + (size_t)kw_begin * HD, n_keys * HD * 2);
-  const int st_row = lane / CH;
-  auto issue = [&](int t) {
-    const int stage = t % DEC_STAGES;
+  // K A-operand of half h, k-step kk: row 16h + col, bytes (32kk + 8q4) * 2 of the row.
+  const int k_off = col * HD * 2 + q4 * 16;
+  // V rows: lane holds chunk (lane % CH) of row (lane / CH) + VROWS * i.
+  const int v_off = (lane / CH) * HD * 2 + (lane % CH) * 16;
+
+  struct Tile {
+    bf16x8 k[2][KSTEPS];
+    bf16x8 v[VLOADS];
+  };
+  auto load = [&](int t, Tile& tl) {
+    const int base = t * DEC_TILE * HD * 2;
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int row = u * RPI + st_row;
-      const int kvo = (row * HD + (((lane % CH) ^ (row & (CH - 1))) * 8)) * 2;
-      const int vvo = (row * HD + (((lane % CH) ^ ((2 * row) & (CH - 1))) * 8)) * 2;
-      const int toff = t * DEC_TILE * HD * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_ptr)(&sm.k[stage][u * RPI * HD]), 16, toff + kvo, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(&sm.v[stage][u * RPI * HD]), 16, toff + vvo, 0, 0, 0);
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) tl.k[h][kk] = buffer_load16_nt(krs, base + k_off + h * 16 * HD * 2 + kk * 64);
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) tl.v[i] = buffer_load16_nt(vrs, base + v_off + i * VROWS * HD * 2);
   };
 
-  // K A-operand: row key = 16*half + col, chunk 4kk + q4 at position ^ swz_k(row).
   // V^T A-operand (transposed read): in 16-lane group q4, source lane 4e + j points at key row
-  // base + 4*q4 + e and column 16cb + 4j; the lane receives column 16cb + col of 4 keys.
+  // base + 4*q4 + e and column 16cb + 4j; the lane receives column 16cb + col of 4 keys. The LDS
+  // tile stores chunk c of row r at position c ^ (2r mod CH): the 8 rows x 2 chunks a 32-lane
+  // read touches fall in distinct banks.
   const int v_e = (lane & 15) >> 2;
   const int v_j = lane & 3;
+  const int st_row = lane / CH;
 
   f32x4 acc[CB];
 #pragma unroll
@@ -143,45 +144,38 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   const float c = scale_log2;
 
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 1) issue(1);
-  for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS));  // only the next tile's loads may be in flight
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("" ::: "memory");  // LDS reads of this tile stay after the wait
-    const int stage = t % DEC_STAGES;
-    const bf16* kt = sm.k[stage];
-    const bf16* vt = sm.v[stage];
+  auto consume = [&](int t, const Tile& tl) {
+    // V tile to LDS (swizzled), consumed below by this wave only.
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int row = i * VROWS + st_row;
+      *reinterpret_cast<bf16x8*>(vt + row * HD + (((lane % CH) ^ ((2 * row) & (CH - 1))) * 8)) = tl.v[i];
+    }
     // S^T for keys 16*half + 4*q4 + r (r = 0..3), column = head.
     f32x4 s[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      s[half] = f32x4{};
-      const int row = 16 * half + col;
+    for (int h = 0; h < 2; ++h) {
+      s[h] = f32x4{};
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + row * HD + (((4 * kk + q4) ^ (row & (CH - 1))) * 8));
-        s[half] = mfma16(a, qf[kk], s[half]);
-      }
+      for (int kk = 0; kk < KSTEPS; ++kk) s[h] = mfma16(tl.k[h][kk], qf[kk], s[h]);
     }
     const int key0 = t * DEC_TILE;  // relative to kw_begin
     float x[8];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 16 * half + 4 * q4 + r;
-        const float v = key < n_keys ? s[half][r] * c : -INFINITY;
-        x[4 * half + r] = v;
+        const int key = key0 + 16 * h + 4 * q4 + r;
+        const float v = key < n_keys ? s[h][r] * c : -INFINITY;
+        x[4 * h + r] = v;
         tmax = fmaxf(tmax, v);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // Tile 0 holds the wave's first key, so m_run is finite after it.
+    // Tile 0 holds the wave's first key, so m_run is finite after it; a fully masked tile
+    // later gives alpha = 1 and p = 0.
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -194,28 +188,34 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
       pb[e] = to_bf16(p);
     }
     l_run = fmaf(l_run, alpha, tsum);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    // Unconditional rescale: a branch here would split the loop body, and the compiler would
+    // then sink the next tile's loads past it and serialise them behind the current tile.
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
-    }
+    for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
     // O^T += V^T P^T: k-slot e < 4 is key 4*q4 + e, e >= 4 is key 16 + 4*q4 + (e - 4).
-    bf16x8 va[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const bf16* p0 = vt + (4 * q4 + v_e) * HD;
-      const bf16* p1 = vt + (16 + 4 * q4 + v_e) * HD;
-      const int c0 = ((2 * cb + (v_j >> 1)) ^ ((2 * (4 * q4 + v_e)) & (CH - 1))) * 8 + 4 * (v_j & 1);
-      const int c1 = ((2 * cb + (v_j >> 1)) ^ ((2 * (16 + 4 * q4 + v_e)) & (CH - 1))) * 8 + 4 * (v_j & 1);
-      va[cb] = tr_pair_async(p0 + c0, p1 + c1);
+      const int r0 = 4 * q4 + v_e;
+      const int r1 = 16 + 4 * q4 + v_e;
+      const bf16* p0 = vt + r0 * HD + (((2 * cb + (v_j >> 1)) ^ ((2 * r0) & (CH - 1))) * 8) + 4 * (v_j & 1);
+      const bf16* p1 = vt + r1 * HD + (((2 * cb + (v_j >> 1)) ^ ((2 * r1) & (CH - 1))) * 8) + 4 * (v_j & 1);
+      acc[cb] = mfma16(__builtin_shufflevector(lds_read_tr(p0), lds_read_tr(p1), 0, 1, 2, 3, 4, 5, 6, 7), pb, acc[cb]);
     }
-    lds_wait_all(va);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma16(va[cb], pb, acc[cb]);
-    if (t + 2 < n_tiles) {
-      // The stage just consumed is refilled: its LDS reads must have completed first.
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt at their maxima
-      asm volatile("" ::: "memory");
-      issue(t + 2);
+  };
+
+  // Two tiles in flight: the loads of tile t + 2 are issued as soon as tile t is consumed. The
+  // loop body is one basic block over a pair of tiles, and the loads are unconditional (tiles
+  // past the wave's keys read as zeros, and a whole tile past the end is fully masked, which
+  // leaves m, l and O unchanged), so the wait before each consume covers only the tile it needs.
+  {
+    Tile ta, tb;
+    load(0, ta);
+    load(1, tb);
+    for (int t = 0; t < n_tiles; t += 2) {
+      consume(t, ta);
+      load(t + 2, ta);
+      consume(t + 1, tb);
+      load(t + 3, tb);
     }
   }
 
@@ -223,8 +223,6 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  __syncthreads();  // every wave is done with its stages; the merge area overlays them
-  DecodeMerge<HD, G>& mg = *reinterpret_cast<DecodeMerge<HD, G>*>(dyn_smem);
   if (col < G) {
     if (q4 == 0) {
       mg.m[w][col] = m_run;  // -inf for a wave with no keys
@@ -232,8 +230,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
     }
     // O^T rows c = 16cb + 4*q4 + r of head column col.
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      *reinterpret_cast<f32x4*>(&mg.o[w][col][16 * cb + 4 * q4]) = acc[cb];
+    for (int cb = 0; cb < CB; ++cb) *reinterpret_cast<f32x4*>(&mg.o[w][col][16 * cb + 4 * q4]) = acc[cb];
   }
   __syncthreads();
   constexpr int PER = HD / 64;
@@ -261,6 +258,21 @@ __global__ __launch_bounds__(DEC_WAVES * 64) void decode_split_kernel(
   }
 }
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+// One wave per (query head, sequence). Lane s holds (m, l) of split s (64 splits per pass), so
+// M, the weights 2^(m_s - M) and L take one round of parallel loads and wave reductions; the
+// output then sums the splits' partial rows with independent loads, PER elements per lane.
 template <int HD>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws,
                                                             const int32_t* __restrict__ kv_len,
@@ -281,19 +293,41 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     return;
   }
   const float* recs = ws + ((size_t)b * H + h) * n_split * REC;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, recs[(size_t)s * REC]);
+  auto ml_of = [&](int s) {
+    return s < ns ? *reinterpret_cast<const float2*>(recs + (size_t)s * REC) : make_float2(-INFINITY, 0.f);
+  };
+  const float2 ml0 = ml_of(lane);
+  float M = ml0.x;
+  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, recs[(size_t)s * REC]);
+  M = wave_max(M);  // finite: every split below ns holds at least one key
   float L = 0.f;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* r = recs + (size_t)s * REC;
-    const float wgt = fast_exp2(r[0] - M);
-    L = fmaf(wgt, r[1], L);
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float2 ml = s0 == 0 ? ml0 : ml_of(s0 + lane);
+    const float wgt = fast_exp2(ml.x - M);  // 0 past ns
+    L = fmaf(wgt, ml.y, L);
+    const int cnt = min(64, ns - s0);
+    // Four splits per step, loads issued together; steps past cnt re-read the last valid
+    // record (the workspace beyond ns is never written) with weight 0.
+    for (int j0 = 0; j0 < cnt; j0 += 4) {
+      float wj[4], v[4][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, r[4 + lane * PER + e], acc[e]);
+      for (int u = 0; u < 4; ++u) {
+        const int j = min(j0 + u, cnt - 1);
+        wj[u] = j0 + u < cnt ? __shfl(wgt, j, 64) : 0.f;
+        const float* r = recs + (size_t)(s0 + j) * REC + 4 + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = r[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj[u], v[u][e], acc[e]);
+    }
   }
+  L = wave_sum(L);
   const float inv = 1.f / L;
 #pragma unroll
   for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bf16(acc[e] * inv);
@@ -305,17 +339,9 @@ hipError_t launch(const void* q, const void* kc, const void* vc, void* o, float*
                   int B, int H, int H_kv, int N_cap, float scale, void* ws, hipStream_t stream,
                   const char* split_name, const char* combine_name) {
   const int n_split = (N_cap + kDecodeSplit - 1) / kDecodeSplit;
-  const size_t smem = decode_smem_bytes<HD>(G);
-  static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_split_kernel<HD, G>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   {
     TimedScope ts(split_name, stream);
-    hipLaunchKernelGGL((decode_split_kernel<HD, G>), dim3(n_split, H_kv, B), dim3(DEC_WAVES * 64), smem, stream,
+    hipLaunchKernelGGL((decode_split_kernel<HD, G>), dim3(B * H_kv, n_split), dim3(DEC_WAVES * 64), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(kc), static_cast<const bf16*>(vc),
                        kv_len, static_cast<float*>(ws), H, H_kv, N_cap, n_split, scale * kLog2e);
   }

@@ -102,6 +102,7 @@ def test_decode_validation(lib):
     assert call(H=30) == INVALID
     assert call(kv=None) == INVALID
     assert call(d=80) == UNSUPPORTED
+    assert call(B=65535, H=512, H_kv=512) == INVALID  # B * H_kv beyond one grid row
     assert lib.attn_decode_workspace_size(1, 1, 1, 96) == 0
 
 

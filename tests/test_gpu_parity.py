@@ -182,6 +182,13 @@ def test_decode_ragged_lengths(lib, H, H_kv, d):
     assert eo <= TOL_BF16 and el <= TOL_BF16
 
 
+def test_decode_more_than_64_splits(lib):
+    # 69 and 65 splits of 1024 keys: the merge takes more than one 64-lane pass over the splits.
+    w = I.Workload("dec_long", "decode", 2, 8, 2, 70000, 64, "bf16", False, seed=18, kv_lo=1, kv_hi=70000)
+    eo, el = decode_check(lib, w, kv_len=[70000, 65601])
+    assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
 def test_decode_zero_length_is_defined(lib):
     w = I.Workload("dec0", "decode", 2, 4, 4, 64, 128, "bf16", False, seed=17, kv_lo=1, kv_hi=64)
     t = I.make_decode(w)
