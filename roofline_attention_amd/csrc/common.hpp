@@ -46,6 +46,19 @@ __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// max(a, b, c) in one v_maximum3_f32 (NaN-propagating maximum; no quieting of the inputs).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// acc + a + b for two bf16 values, in one v_dot2c_f32_bf16 against (1, 1).
+__device__ __forceinline__ float bf16_pair_sum(bf16 a, bf16 b, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t x = {a, b};
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+}
+
 // Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane gets the total.
 __device__ __forceinline__ float row16_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));  // xor 1

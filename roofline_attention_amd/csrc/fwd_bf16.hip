@@ -209,25 +209,36 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   // returns P^T in the B-operand layout (k-step ks = 2kb + hh takes accumulator slots 8hh..8hh+7).
   // The output rescale, needed only when the maximum rises, is left to the caller.
   auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4], float& alpha) {
-    float mx[8];
+    // Row maximum over the 32 scores as a tree of 3-input maxima. fmaximum (NaN-propagating)
+    // equals fmaxf on the finite or -inf scores here and needs no NaN-quieting of its inputs.
+    float m1[11];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) mx[i] = fmaxf(fmaxf(s[0][2 * i], s[0][2 * i + 1]), fmaxf(s[1][2 * i], s[1][2 * i + 1]));
-    const float rmax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])), fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+    for (int i = 0; i < 10; ++i) {
+      const int a = 3 * i, b = 3 * i + 1, c3 = 3 * i + 2;
+      m1[i] = vmax3(s[a >> 4][a & 15], s[b >> 4][b & 15], s[c3 >> 4][c3 & 15]);
+    }
+    m1[10] = __builtin_elementwise_maximum(s[1][14], s[1][15]);
+    const float m2a = vmax3(m1[0], m1[1], m1[2]), m2b = vmax3(m1[3], m1[4], m1[5]);
+    const float m2c = vmax3(m1[6], m1[7], m1[8]), m2d = __builtin_elementwise_maximum(m1[9], m1[10]);
+    const float rmax = vmax3(m2a, m2b, __builtin_elementwise_maximum(m2c, m2d));
     // Tile 0 always holds key 0, which every query row keeps, so m_run is finite after it.
     const float tmax = pair_max(rmax) * c;
     const bool raise = tmax > m_run + kLazyRescale;
     const float m_new = raise ? tmax : m_run;
     alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
-    float tsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kb][r], c, -m_new));
-        tsum += p;
-        pf[2 * kb + (r >> 3)][r & 7] = to_bf16(p);
-      }
+      for (int r = 0; r < 16; ++r) pf[2 * kb + (r >> 3)][r & 7] = to_bf16(fast_exp2(fmaf(s[kb][r], c, -m_new)));
+    }
+    // The normaliser sums the same bf16-rounded probabilities that multiply V, two per
+    // instruction (bf16 dot product with (1, 1), fp32 accumulation).
+    float tsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) tsum = bf16_pair_sum(pf[i][e], pf[i][e + 1], tsum);
     }
     l_run = fmaf(l_run, alpha, tsum);
     // The branch condition reads tsum so the exponentials stay ahead of the (rare) rescale branch,

@@ -64,7 +64,7 @@ def test_f32_shapes(lib, B, H, H_kv, N, d, causal):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 333, 128), (1, 2, 2, 333, 64), (2, 8, 2, 200, 128),
                                            (1, 4, 1, 65, 64), (1, 2, 2, 1, 128), (1, 1, 1, 129, 128),
-                                           (1, 2, 2, 512, 64)])
+                                           (1, 2, 2, 512, 64), (1, 2, 2, 600, 128), (1, 1, 1, 257, 64)])
 def test_bf16_shapes(lib, B, H, H_kv, N, d, causal):
     w = I.Workload("bf16_case", "fwd", B, H, H_kv, N, d, "bf16", causal, seed=12)
     t, o, lse = run_fwd(lib, w)
