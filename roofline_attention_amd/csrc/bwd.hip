@@ -12,7 +12,7 @@
 // Kernels, per (batch, head):
 //   bwd_pre : D_i = sum_t dO[i,t] * O[i,t]   (equals sum_j P_ij dP_ij)
 //   bwd_dkdv: workgroup = 128 keys (4 waves x 32, K and V of its keys in registers); streams
-//             64-query tiles of Q, dO, LSE and D through double-buffered LDS:
+//             64-query tiles of Q, dO, LSE and D through three LDS stages:
 //             S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e), dV += P^T dO, dP = dO V^T,
 //             dS = P (dP - D), dK += dS^T Q; stores dK * scale and dV.
 //   bwd_dq  : workgroup = 128 queries (4 waves x 32, Q and dO of its rows in registers); streams
@@ -103,14 +103,29 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, const TrLane<HD, 
 
 // ------------------------------------------------------------------------------ dK dV ----
 
+constexpr int DKDV_STAGES = 3;  // query tiles resident in LDS: one read, one in flight, one draining
+
 template <int HD>
 struct DkdvSmem {
-  bf16 q[2][BWD_BQ * HD];
-  bf16 dO[2][BWD_BQ * HD];
-  float lse[2][BWD_BQ];
-  float dd[2][BWD_BQ];
+  bf16 q[DKDV_STAGES][BWD_BQ * HD];
+  bf16 dO[DKDV_STAGES][BWD_BQ * HD];
+  float lse[DKDV_STAGES][BWD_BQ];
+  float dd[DKDV_STAGES][BWD_BQ];
 };
 
+// Work is cut into 32-query blocks u (block u = query rows 32u .. 32u + 31, half u % 2 of query
+// tile u / 2), each in three parts:
+//   A(u): S and dP accumulators for the wave's 32 keys (16 MFMAs on row operands of the tile),
+//   V(u): P = 2^(S c - LSE log2 e) and dS = P (dP - D), rounded to bf16 (vector ALUs),
+//   B(u): dV += P^T dO and dK += dS^T Q (16 MFMAs on transposed operands of the tile).
+// A step issues A(u+1), V(u) and B(u-1): three independent chains that the wave interleaves. (On
+// gfx950 a vector instruction overlaps a running MFMA only when both come from the same wave, so
+// the exponentials of one block must sit between the MFMAs of its neighbours.) Query tiles rotate
+// through three LDS stages: tile t is read from step 2t-1 (by A) to step 2t+2 (by B), and tile t+2
+// is loaded into the stage of tile t-1 right after the barrier between tile t's two steps.
+// Causal workgroups run their first two query tiles (the ones crossing the diagonal of some wave)
+// block by block with the mask, and the pipeline from the third tile on, where no key of the
+// workgroup follows any query.
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -161,65 +176,113 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
   const bf16* dOh = dO + head;
   const float* LSEh = LSE + rowbase;
   const float* Dh = Dg + rowbase;
+  const int n_qt = (N + BWD_BQ - 1) / BWD_BQ;
 
-  auto stage = [&](int qt, int s) {
+  auto stage_of = [](int t) { return (t + DKDV_STAGES) % DKDV_STAGES; };  // t >= -1
+  auto stage = [&](int qt) {
+    const int s = stage_of(qt);
     const int r0 = qt * BWD_BQ;
     stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(Qh, r0, N, sm.q[s], w, lane);
     stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(dOh, r0, N, sm.dO[s], w, lane);
-    if (w == 0) load_to_lds<4>(make_rsrc(LSEh + r0, (N - r0) * 4), lane * 4, sm.lse[s]);
-    if (w == 1) load_to_lds<4>(make_rsrc(Dh + r0, (N - r0) * 4), lane * 4, sm.dd[s]);
+    if (w == 0) load_to_lds<4>(dma_rsrc(LSEh + r0, (N - r0) * 4), lane * 4, sm.lse[s]);
+    if (w == 1) load_to_lds<4>(dma_rsrc(Dh + r0, (N - r0) * 4), lane * 4, sm.dd[s]);
+  };
+  // Barrier between the two steps of tile t: this wave's loads of tile t+1 have landed and every
+  // wave's reads of tile t-1 have returned; then tile t+2 goes into tile t-1's stage.
+  auto mid = [&](int t) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t + 2 < n_qt) stage(t + 2);
   };
 
-  const int n_qt = (N + BWD_BQ - 1) / BWD_BQ;
-  const int first_qt = CAUSAL ? (kt * 128) / BWD_BQ : 0;
-  stage(first_qt, first_qt & 1);
-  for (int qt = first_qt; qt < n_qt; ++qt) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // tile qt is in LDS everywhere; the other stage is free
-    if (qt + 1 < n_qt) stage(qt + 1, (qt + 1) & 1);
-    const int s = qt & 1;
-    const bf16* qtile = sm.q[s];
-    const bf16* dtile = sm.dO[s];
+  auto blk_A = [&](int u, f32x16& sacc, f32x16& dpacc) {
+    const int s = stage_of(u >> 1);
+    const bf16* qrow = sm.q[s] + (u & 1) * 32 * HD + row_off;
+    const bf16* drow = sm.dO[s] + (u & 1) * 32 * HD + row_off;
+    sacc = f32x16{};
+    dpacc = f32x16{};
 #pragma unroll
-    for (int qb = 0; qb < BWD_BQ / 32; ++qb) {
-      const int i0 = qt * BWD_BQ + qb * 32;
-      if (CAUSAL && i0 + 31 < kw0) continue;  // every query of the block precedes every key of the wave
-      // S and dP: lane column = key, rows = queries i0 + 8(r/4) + 4g + r%4.
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
-      const bf16* qrow = qtile + qb * 32 * HD + row_off;
-      const bf16* drow = dtile + qb * 32 * HD + row_off;
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int off = ((2 * kk) ^ row_t) * 8;
+      sacc = mfma32(*reinterpret_cast<const bf16x8*>(qrow + off), kf[kk], sacc);
+      dpacc = mfma32(*reinterpret_cast<const bf16x8*>(drow + off), vf[kk], dpacc);
+    }
+  };
+  // S, dP lanes: column = key, rows = queries 32u + 8(r/4) + 4g + r%4. P^T and dS^T leave in the
+  // A-operand layout of B (lane row = key, k-step hh covers queries 16hh + {4g..4g+3, 8+4g..}).
+  auto blk_V = [&](int u, const f32x16& sacc, const f32x16& dpacc, bf16x8 (&pb)[2], bf16x8 (&dsb)[2],
+                   bool mask) {
+    const int s = stage_of(u >> 1);
+    const int qb = u & 1;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int off = ((2 * kk) ^ row_t) * 8;
-        sacc = mfma32(*reinterpret_cast<const bf16x8*>(qrow + off), kf[kk], sacc);
-        dpacc = mfma32(*reinterpret_cast<const bf16x8*>(drow + off), vf[kk], dpacc);
-      }
-      const bool diag = CAUSAL && i0 < kw0 + 32;  // some key of the wave follows some query of the block
-      bf16x8 pb[2], dsb[2];
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[s][qb * 32 + 8 * rg + 4 * g]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[s][qb * 32 + 8 * rg + 4 * g]);
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[s][qb * 32 + 8 * rg + 4 * g]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[s][qb * 32 + 8 * rg + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rg + e;
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e] * kLog2e));
-          if (diag && key > i0 + 8 * rg + 4 * g + e) p = 0.f;
-          pb[r >> 3][r & 7] = to_bf16(p);
-          dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - d4[e]));
-        }
-      }
-      // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane row = key, k-step hh covers queries
-      // 16hh + {4g..4g+3, 8+4g..8+4g+3}); B = dO / Q columns 32cb + l32 by transposed read.
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-          dv[cb] = mfma32(pb[hh], tr_operand<HD>(dtile, tl, qb * 32 + 16 * hh, cb), dv[cb]);
-          dk[cb] = mfma32(dsb[hh], tr_operand<HD>(qtile, tl, qb * 32 + 16 * hh, cb), dk[cb]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * rg + e;
+        float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e] * kLog2e));
+        if (mask && key > 32 * u + 8 * rg + 4 * g + e) p = 0.f;
+        pb[r >> 3][r & 7] = to_bf16(p);
+        dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - d4[e]));
       }
     }
+  };
+  // B operands: dO / Q columns 32cb + l32 by transposed read.
+  auto blk_B = [&](int u, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
+    const int s = stage_of(u >> 1);
+    const int r0 = (u & 1) * 32;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) {
+        dv[cb] = mfma32(pb[hh], tr_operand<HD>(sm.dO[s], tl, r0 + 16 * hh, cb), dv[cb]);
+        dk[cb] = mfma32(dsb[hh], tr_operand<HD>(sm.q[s], tl, r0 + 16 * hh, cb), dk[cb]);
+      }
+    }
+  };
+
+  const int t_first = CAUSAL ? (kt * 128) / BWD_BQ : 0;
+  if (!CAUSAL) {
+    // The pipeline's first step applies B to block -1 with zero P and dS; its stage must hold
+    // finite values (0 * NaN would poison the accumulators).
+    const int s = stage_of(-1);
+    bf16x8* zq = reinterpret_cast<bf16x8*>(sm.q[s]);
+    bf16x8* zd = reinterpret_cast<bf16x8*>(sm.dO[s]);
+    for (int i = tid; i < BWD_BQ * HD / 8; i += BWD_THREADS) zq[i] = zd[i] = bf16x8{};
+  }
+  stage(t_first);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (t_first + 1 < n_qt) stage(t_first + 1);
+
+  int t = t_first;
+  if (CAUSAL) {
+    for (; t < min(n_qt, t_first + 2); ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1) mid(t);
+        f32x16 sacc, dpacc;
+        bf16x8 pb[2], dsb[2];
+        blk_A(2 * t + h, sacc, dpacc);
+        blk_V(2 * t + h, sacc, dpacc, pb, dsb, true);
+        blk_B(2 * t + h, pb, dsb);
+      }
+    }
+  }
+  if (t < n_qt) {
+    f32x16 sa, da, sb, db;
+    bf16x8 pc[2], dc[2], pp[2], dpp[2];
+    pp[0] = pp[1] = dpp[0] = dpp[1] = bf16x8{};
+    blk_A(2 * t, sa, da);
+    for (; t < n_qt; ++t) {
+      blk_A(2 * t + 1, sb, db);
+      blk_V(2 * t, sa, da, pc, dc, false);
+      blk_B(2 * t - 1, pp, dpp);
+      mid(t);
+      blk_A(2 * t + 2, sa, da);  // past the last tile this reads a drained stage; the result is unused
+      blk_V(2 * t + 1, sb, db, pp, dpp, false);
+      blk_B(2 * t, pc, dc);
+    }
+    blk_B(2 * n_qt - 1, pp, dpp);
   }
 
   // dK/dV accumulators: lane column c = 32cb + l32, rows = keys kw0 + 8(r/4) + 4g + r%4.

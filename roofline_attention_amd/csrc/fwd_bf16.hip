@@ -31,6 +31,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tile.hpp"
 
 namespace ra {
 namespace {
@@ -55,25 +56,6 @@ template <int HD>
 __device__ __forceinline__ int swz_v(int r) {
   if constexpr (HD == 128) return 4 * (r & 3) + 2 * ((r >> 1) & 1);
   else return (2 * r) & 7;
-}
-
-typedef void __attribute__((address_space(3))) * lds_void_ptr;
-typedef bf16x4 __attribute__((address_space(3))) * lds_bf16x4_ptr;
-
-// Buffer resource over `bytes` bytes from `base` (raw buffer, 32-bit byte offsets). Loads at or
-// beyond `bytes` return zero without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
-// One 16-byte-per-lane direct load into LDS: lane i of the wave writes lds_block + 16 i with the
-// bytes at voffset of the resource (buffer_load_dwordx4 ... lds).
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset, void* lds_block) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds_block, 16, voffset, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
 }
 
 // max over the lane pair (l, l ^ 32) that shares one query row
@@ -149,17 +131,17 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const bf16* v_head = V + kv_head;
   auto issue_k = [&](int kt, int stage) {
     const int row0 = kt * FWD_BC;
-    const auto rsrc = make_rsrc(k_head + (size_t)row0 * HD, (N - row0) * HD * 2);
+    const u32x4 rsrc = dma_rsrc(k_head + (size_t)row0 * HD, (N - row0) * HD * 2);
 #pragma unroll
     for (int u = 0; u < BLOCKS / 4; ++u)
-      load_to_lds(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * 4 + w) * RPI * HD]);
+      load_to_lds<16>(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * 4 + w) * RPI * HD]);
   };
   auto issue_v = [&](int kt, int stage) {
     const int row0 = kt * FWD_BC;
-    const auto rsrc = make_rsrc(v_head + (size_t)row0 * HD, (N - row0) * HD * 2);
+    const u32x4 rsrc = dma_rsrc(v_head + (size_t)row0 * HD, (N - row0) * HD * 2);
 #pragma unroll
     for (int u = 0; u < BLOCKS / 4; ++u)
-      load_to_lds(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * 4 + w) * RPI * HD]);
+      load_to_lds<16>(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * 4 + w) * RPI * HD]);
   };
 
   // K A-operand read (S^T block kb, k-step kk): row 32kb + l32, chunk 2kk + g at position

@@ -42,48 +42,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes < 0 ? 0 : bytes, 0x00020000);
 }
 
-// Direct load into LDS: lane i of the wave writes lds_block + SIZE * i with the SIZE bytes at
-// byte offset voffset of the resource.
+// The same resource as its four descriptor words (base address, stride 0, byte count, raw-buffer
+// flags), wave-uniform, for the direct-to-LDS loads below.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < 0 ? 0 : bytes));
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Direct load into LDS: lane i of the wave writes lds_block + SIZE * i with the SIZE bytes at byte
+// offset voffset of the resource (buffer_load_dword[x4] ... lds; M0 holds the LDS block address,
+// which must be wave-uniform). Issued as inline assembly on purpose: the compiler's wait insertion
+// models the builtin form as a write that may alias every later LDS read and waits for all such
+// loads in flight (vmcnt(0)) before the next LDS read, which would expose the latency of a tile
+// prefetched across the reads of the current one. Callers therefore order these loads
+// themselves: a tile is read only after s_waitcnt vmcnt(0) and a workgroup barrier.
 template <int SIZE>
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t rsrc, int voffset, void* lds_block) {
+__device__ __forceinline__ void load_to_lds(const u32x4& rsrc, int voffset, const void* lds_block) {
   static_assert(SIZE == 16 || SIZE == 4, "dwordx4 or dword");
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_block;
   if constexpr (SIZE == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds_block, 16, voffset, 0, 0, 0);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0) : "memory");
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)lds_block, 4, voffset, 0, 0, 0);
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0) : "memory");
 }
 
 // Transposing read: in each 16-lane group, lane 4e + j supplies the address of 4 bf16 at row e
 // of a 4-row block; lane i of the group receives the 4 elements of column i of that block.
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
-}
-
-// The same read issued as inline assembly. The compiler's wait insertion treats the builtin form
-// as aliasing every direct-to-LDS load still in flight and waits for all of them (vmcnt(0)); a
-// kernel that keeps the next tile's loads in flight across its reads of the current tile uses this
-// form instead and orders it itself: the result may be used only after lds_wait(), which waits
-// for all of this wave's LDS reads and ties the results so that no use is scheduled earlier.
-__device__ __forceinline__ bf16x4 lds_read_tr_async(const bf16* p) {
-  bf16x4 r;
-  const unsigned addr = (unsigned)(uintptr_t)((const bf16 __attribute__((address_space(3)))*)p);
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 tr_pair_async(const bf16* p0, const bf16* p1) {
-  return __builtin_shufflevector(lds_read_tr_async(p0), lds_read_tr_async(p1), 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-template <int N>
-__device__ __forceinline__ void lds_wait_all(bf16x8 (&a)[N]) {
-  static_assert(N == 4 || N == 8, "operand batch");
-  if constexpr (N == 4) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
-  } else {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
-                 "+v"(a[6]), "+v"(a[7]));
-  }
 }
 
 // Stages ROWS x HD bf16 rows [row0, row0 + ROWS) of a row-major [n_rows, HD] matrix into an LDS
@@ -96,7 +88,7 @@ __device__ __forceinline__ void stage_tile(const bf16* __restrict__ src, int row
   constexpr int RPI = 1024 / (HD * 2);
   constexpr int BLOCKS = ROWS / RPI;
   static_assert(BLOCKS % NWAVES == 0, "tile geometry");
-  const auto rsrc = make_rsrc(src + (size_t)row0 * HD, (n_rows - row0) * HD * 2);
+  const u32x4 rsrc = dma_rsrc(src + (size_t)row0 * HD, (n_rows - row0) * HD * 2);
 #pragma unroll
   for (int u = 0; u < BLOCKS / NWAVES; ++u) {
     const int blk = u * NWAVES + w;
