@@ -99,8 +99,11 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
  * of the MoA paper, "Validating Memory-Optimal Transformer Kernels on Real Hardware", section 4.5).
  *   q, k, v, o, dout: bf16 in the layouts above; o and lse must come from attn_fwd on the same
  *   q, k, v, causal and scale. dq [B,H,N,d], dk, dv [B,H_kv,N,d]: float32, fully overwritten.
+ *   Grouped heads (H_kv < H, H % H_kv == 0): the dK/dV of a KV head sum the contributions of its
+ *   H / H_kv query heads, accumulated by the one workgroup that owns those rows (no K/V expansion,
+ *   "Why Fast GPUs Still Wait for Memory", section "Attention III - KV cache, GQA, MLA").
  *   workspace: at least attn_bwd_workspace_size(B, H, N, d) bytes, 16-byte aligned, scratch.
- * dtype must be ATTN_BF16. H_kv must equal H (grouped-query backward is not provided).
+ * dtype must be ATTN_BF16.
  */
 size_t attn_bwd_workspace_size(int B, int H, int N, int d);
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -159,7 +159,10 @@ def bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
 
 def bwd(q, k, v, o, dout, lse, causal: bool, scale: Optional[float] = None, dq=None, dk=None, dv=None,
         workspace: Optional[torch.Tensor] = None):
-    """Backward: bf16 q, k, v, o, dout [B,H,N,d] and fp32 lse [B,H,N] from fwd. Returns fp32 (dq, dk, dv)."""
+    """Backward: bf16 q, o, dout [B,H,N,d], k, v [B,H_kv,N,d] and fp32 lse [B,H,N] from fwd.
+
+    Returns fp32 (dq [B,H,N,d], dk, dv [B,H_kv,N,d]); under grouped heads dk, dv sum over each KV
+    head's query heads."""
     _need(q, "q", torch.bfloat16)
     B, H, N, d = q.shape
     H_kv = k.shape[1]

@@ -222,7 +222,6 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   attn_status st = check_shape(B, H, H_kv, N, d, scale);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "backward supports ATTN_BF16 only");
-  if (H_kv != H) return fail(ATTN_ERR_UNSUPPORTED, "backward requires H_kv == H");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv))
     return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
@@ -232,16 +231,17 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const long long tiles = (long long)((N + 127) / 128) * H * B;
   if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
-  const size_t tb = (size_t)B * H * N * d * 2, gb = (size_t)B * H * N * d * 4, lb = (size_t)B * H * N * 4;
-  const Range ins[] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dout, tb}, {lse, lb}};
-  const Range outs[] = {{dq, gb}, {dk, gb}, {dv, gb}, {workspace, need}};
+  const size_t tb = (size_t)B * H * N * d * 2, kb = (size_t)B * H_kv * N * d * 2, gb = (size_t)B * H * N * d * 4,
+               gkb = (size_t)B * H_kv * N * d * 4, lb = (size_t)B * H * N * 4;
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}, {o, tb}, {dout, tb}, {lse, lb}};
+  const Range outs[] = {{dq, gb}, {dk, gkb}, {dv, gkb}, {workspace, need}};
   for (const Range& a : outs)
     for (const Range& b : ins)
       if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
   for (int i = 0; i < 4; ++i)
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
-  return hip_status(ra::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal != 0, scale, workspace,
+  return hip_status(ra::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal != 0, scale, workspace,
                                    static_cast<hipStream_t>(stream)));
 }
 

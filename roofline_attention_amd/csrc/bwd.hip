@@ -130,7 +130,8 @@ template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dK, float* __restrict__ dV, int N, int n_ktiles, float scale, float scale_log2) {
+    float* __restrict__ dK, float* __restrict__ dV, int H, int group, int N, int n_ktiles, float scale,
+    float scale_log2) {
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
   DkdvSmem<HD>& sm = *reinterpret_cast<DkdvSmem<HD>*>(dyn_smem);
   constexpr int KSTEPS = HD / 16;
@@ -138,15 +139,17 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
 
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = item % n_ktiles;  // causal: low key tiles see the most query tiles and go first
-  const int bh = item / n_ktiles;
+  const int bhk = item / n_ktiles;  // (sequence, KV head)
+  const int Hkv = H / group;
+  const int b = bhk / Hkv;
+  const int hk = bhk % Hkv;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const size_t head = (size_t)bh * N * HD;
-  const size_t rowbase = (size_t)bh * N;
+  const size_t head = (size_t)bhk * N * HD;  // K, V, dK, dV rows of this KV head
   const int kw0 = kt * 128 + w * 32;  // this wave's first key
   const int key = kw0 + l32;          // the key column this lane holds in S and dP
 
@@ -172,10 +175,11 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
   // Row-operand reads (A = Q or dO rows of a 32-query block): row qb*32 + l32, chunk 2kk + g.
   const int row_t = g ^ swz_both<HD>(l32);  // swz_both repeats every 16 rows
   const int row_off = l32 * HD;
-  const bf16* Qh = Q + head;
-  const bf16* dOh = dO + head;
-  const float* LSEh = LSE + rowbase;
-  const float* Dh = Dg + rowbase;
+  // Query-side rows of the query head currently streamed (set per head of the group below).
+  const bf16* Qh = nullptr;
+  const bf16* dOh = nullptr;
+  const float* LSEh = nullptr;
+  const float* Dh = nullptr;
   const int n_qt = (N + BWD_BQ - 1) / BWD_BQ;
 
   auto stage_of = [](int t) { return (t + DKDV_STAGES) % DKDV_STAGES; };  // t >= -1
@@ -241,48 +245,60 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
     }
   };
 
-  const int t_first = CAUSAL ? (kt * 128) / BWD_BQ : 0;
-  if (!CAUSAL) {
-    // The pipeline's first step applies B to block -1 with zero P and dS; its stage must hold
-    // finite values (0 * NaN would poison the accumulators).
-    const int s = stage_of(-1);
-    bf16x8* zq = reinterpret_cast<bf16x8*>(sm.q[s]);
-    bf16x8* zd = reinterpret_cast<bf16x8*>(sm.dO[s]);
-    for (int i = tid; i < BWD_BQ * HD / 8; i += BWD_THREADS) zq[i] = zd[i] = bf16x8{};
-  }
-  stage(t_first);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (t_first + 1 < n_qt) stage(t_first + 1);
+  // The group's query heads run one after another over the same K/V rows; dK and dV accumulate
+  // across them in registers, so each element is still written once.
+  for (int j = 0; j < group; ++j) {
+    const size_t qrows = (size_t)b * H + (size_t)hk * group + j;
+    Qh = Q + qrows * N * HD;
+    dOh = dO + qrows * N * HD;
+    LSEh = LSE + qrows * N;
+    Dh = Dg + qrows * N;
+    // Every wave has finished reading the previous head's tiles before this head's prologue
+    // writes LDS.
+    if (j > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int t_first = CAUSAL ? (kt * 128) / BWD_BQ : 0;
+    if (!CAUSAL) {
+      // The pipeline's first step applies B to block -1 with zero P and dS; its stage must hold
+      // finite values (0 * NaN would poison the accumulators).
+      const int s = stage_of(-1);
+      bf16x8* zq = reinterpret_cast<bf16x8*>(sm.q[s]);
+      bf16x8* zd = reinterpret_cast<bf16x8*>(sm.dO[s]);
+      for (int i = tid; i < BWD_BQ * HD / 8; i += BWD_THREADS) zq[i] = zd[i] = bf16x8{};
+    }
+    stage(t_first);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (t_first + 1 < n_qt) stage(t_first + 1);
 
-  int t = t_first;
-  if (CAUSAL) {
-    for (; t < min(n_qt, t_first + 2); ++t) {
+    int t = t_first;
+    if (CAUSAL) {
+      for (; t < min(n_qt, t_first + 2); ++t) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h == 1) mid(t);
-        f32x16 sacc, dpacc;
-        bf16x8 pb[2], dsb[2];
-        blk_A(2 * t + h, sacc, dpacc);
-        blk_V(2 * t + h, sacc, dpacc, pb, dsb, true);
-        blk_B(2 * t + h, pb, dsb);
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1) mid(t);
+          f32x16 sacc, dpacc;
+          bf16x8 pb[2], dsb[2];
+          blk_A(2 * t + h, sacc, dpacc);
+          blk_V(2 * t + h, sacc, dpacc, pb, dsb, true);
+          blk_B(2 * t + h, pb, dsb);
+        }
       }
     }
-  }
-  if (t < n_qt) {
-    f32x16 sa, da, sb, db;
-    bf16x8 pc[2], dc[2], pp[2], dpp[2];
-    pp[0] = pp[1] = dpp[0] = dpp[1] = bf16x8{};
-    blk_A(2 * t, sa, da);
-    for (; t < n_qt; ++t) {
-      blk_A(2 * t + 1, sb, db);
-      blk_V(2 * t, sa, da, pc, dc, false);
-      blk_B(2 * t - 1, pp, dpp);
-      mid(t);
-      blk_A(2 * t + 2, sa, da);  // past the last tile this reads a drained stage; the result is unused
-      blk_V(2 * t + 1, sb, db, pp, dpp, false);
-      blk_B(2 * t, pc, dc);
+    if (t < n_qt) {
+      f32x16 sa, da, sb, db;
+      bf16x8 pc[2], dc[2], pp[2], dpp[2];
+      pp[0] = pp[1] = dpp[0] = dpp[1] = bf16x8{};
+      blk_A(2 * t, sa, da);
+      for (; t < n_qt; ++t) {
+        blk_A(2 * t + 1, sb, db);
+        blk_V(2 * t, sa, da, pc, dc, false);
+        blk_B(2 * t - 1, pp, dpp);
+        mid(t);
+        blk_A(2 * t + 2, sa, da);  // past the last tile this reads a drained stage; the result is unused
+        blk_V(2 * t + 1, sb, db, pp, dpp, false);
+        blk_B(2 * t, pc, dc);
+      }
+      blk_B(2 * n_qt - 1, pp, dpp);
     }
-    blk_B(2 * n_qt - 1, pp, dpp);
   }
 
   // dK/dV accumulators: lane column c = 32cb + l32, rows = keys kw0 + 8(r/4) + 4g + r%4.
@@ -311,7 +327,7 @@ template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dQ, int N, int n_qtiles, float scale, float scale_log2) {
+    float* __restrict__ dQ, int H, int group, int N, int n_qtiles, float scale, float scale_log2) {
   __shared__ DqSmem<HD> sm;
   constexpr int KSTEPS = HD / 16;
   constexpr int CBLK = HD / 32;
@@ -326,8 +342,9 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const size_t head = (size_t)bh * N * HD;
+  const size_t head = (size_t)bh * N * HD;  // Q, dO, dQ rows of this query head
   const size_t rowbase = (size_t)bh * N;
+  const size_t kv_head = ((size_t)(bh / H) * (H / group) + (bh % H) / group) * N * HD;
   const int q0 = qt * 128 + w * 32;
   const int qi = q0 + l32;
 
@@ -356,8 +373,8 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
   const int krow_t = g ^ swz_both<HD>(l32);
   const int vrow_t = g ^ swz_rows<HD>(l32);
   const int row_off = l32 * HD;
-  const bf16* Kh = K + head;
-  const bf16* Vh = V + head;
+  const bf16* Kh = K + kv_head;
+  const bf16* Vh = V + kv_head;
 
   auto stage = [&](int t, int s) {
     stage_tile<HD, BWD_BK, 4, swz_both<HD>>(Kh, t * BWD_BK, N, sm.k[s], w, lane);
@@ -418,8 +435,8 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
 
 template <int HD, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, float scale,
-                  void* ws, hipStream_t stream, const char* pre_name, const char* dkdv_name,
+                  const float* lse, float* dq, float* dk, float* dv, int B, int H, int H_kv, int N,
+                  float scale, void* ws, hipStream_t stream, const char* pre_name, const char* dkdv_name,
                   const char* dq_name) {
   const bf16* Q = static_cast<const bf16*>(q);
   const bf16* K = static_cast<const bf16*>(k);
@@ -437,7 +454,8 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_t = (N + 127) / 128;
-  const unsigned total = (unsigned)((long long)n_t * H * B);
+  const unsigned total = (unsigned)((long long)n_t * H * B);        // dQ: per query head
+  const unsigned total_kv = (unsigned)((long long)n_t * H_kv * B);  // dK, dV: per KV head
   const size_t dkdv_smem = sizeof(DkdvSmem<HD>);
   static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
   if (!attr_set) {
@@ -448,15 +466,15 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   }
   {
     TimedScope ts(dkdv_name, stream);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), dkdv_smem, stream, Q, K, V,
-                       dO, lse, D, dk, dv, N, n_t, scale, scale * kLog2e);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total_kv), dim3(BWD_THREADS), dkdv_smem, stream, Q, K,
+                       V, dO, lse, D, dk, dv, H, H / H_kv, N, n_t, scale, scale * kLog2e);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   {
     TimedScope ts(dq_name, stream);
     hipLaunchKernelGGL((bwd_dq_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, stream, Q, K, V, dO, lse,
-                       D, dq, N, n_t, scale, scale * kLog2e);
+                       D, dq, H, H / H_kv, N, n_t, scale, scale * kLog2e);
   }
   return hipGetLastError();
 }
@@ -469,17 +487,17 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, float* dq, float* dk, float* dv, int B, int H, int N, int d,
+                      const float* lse, float* dq, float* dk, float* dv, int B, int H, int H_kv, int N, int d,
                       bool causal, float scale, void* ws, hipStream_t stream) {
   if (d == 128) {
-    return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, scale, ws, stream,
+    return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
                                       "bwd_pre_d128", "bwd_dkdv_d128_causal", "bwd_dq_d128_causal")
-                  : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, scale, ws, stream,
+                  : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
                                        "bwd_pre_d128", "bwd_dkdv_d128", "bwd_dq_d128");
   }
-  return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, scale, ws, stream,
+  return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
                                    "bwd_pre_d64", "bwd_dkdv_d64_causal", "bwd_dq_d64_causal")
-                : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, scale, ws, stream,
+                : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
                                     "bwd_pre_d64", "bwd_dkdv_d64", "bwd_dq_d64");
 }
 

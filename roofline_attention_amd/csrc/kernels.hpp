@@ -42,7 +42,7 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, float* dq, float* dk, float* dv,
-                      int B, int H, int N, int d, bool causal, float scale, void* ws,
+                      int B, int H, int H_kv, int N, int d, bool causal, float scale, void* ws,
                       hipStream_t stream);
 
 }  // namespace ra

@@ -116,7 +116,7 @@ def test_bwd_validation(lib):
                             dtype, p[9], ws_bytes, None)
 
     assert call(ws_bytes=need - 4) == WORKSPACE
-    assert call(H_kv=4) == UNSUPPORTED
+    assert call(H_kv=5) == INVALID  # 16 query heads do not split into 5 groups
     assert call(dtype=F32) == UNSUPPORTED
     assert call(lse=None) == INVALID
 

@@ -211,10 +211,13 @@ def bwd_case(lib, w):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 128), (1, 2, 200, 128), (2, 2, 333, 64), (1, 1, 1, 128),
-                                      (1, 2, 65, 64)])
-def test_bwd_shapes(lib, B, H, N, d, causal):
-    w = I.Workload("bwd_case", "fwdbwd", B, H, H, N, d, "bf16", causal, seed=18)
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 256, 128), (1, 2, 2, 200, 128), (2, 2, 2, 333, 64),
+                                           (1, 1, 1, 1, 128), (1, 2, 2, 65, 64),
+                                           # grouped heads: dK/dV sum over each KV head's query heads
+                                           (1, 4, 2, 600, 128), (2, 8, 2, 333, 64), (1, 4, 1, 200, 128),
+                                           (1, 8, 1, 129, 64)])
+def test_bwd_shapes(lib, B, H, H_kv, N, d, causal):
+    w = I.Workload("bwd_case", "fwdbwd", B, H, H_kv, N, d, "bf16", causal, seed=18)
     t, o, dq, dk, dv = bwd_case(lib, w)
     rdq, rdk, rdv, ro, _ = orc.attention_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), causal, w.scale)
     errs = [max_err(o, ro), max_err(dq, rdq), max_err(dk, rdk), max_err(dv, rdv)]
