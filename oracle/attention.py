@@ -22,6 +22,9 @@ design notes):
     (section "Attention III - KV cache, GQA, MLA" gives only g = h / h_kv);
   * LSE is the natural-log log-sum-exp of each score row over unmasked keys;
   * decode is one query row against the first kv_len[b] cache rows;
+  * a ragged (variable-length) batch packs its sequences' rows one after another
+    ([T, H, d], offsets cu_seqlens); each sequence attends only within itself, and a
+    causal position is counted from the sequence's first row;
   * the backward pass is the gradient of L = sum(O * dO) with respect to Q, K
     and V, recomputing P from an explicit S (same page: "the backward pass does
     more arithmetic, because S is recomputed rather than stored"; the MoA paper,
@@ -101,6 +104,62 @@ def attention_fwd_rows(q, k, v, causal: bool, scale: float, rows):
         s = scale * (k[b, hk, :n_keys] @ q[b, h, i])
         p, lse_r = _softmax_rows(s[None, :])
         o[r] = p[0] @ v[b, hk, :n_keys]
+        lse[r] = lse_r[0]
+    return o, lse
+
+
+def attention_fwd_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
+    """Variable-length (ragged) prefill over packed token rows.
+
+    q [T, H, d], k/v [T, H_kv, d]; sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1] - 1
+    and attends only within itself, with positions counted from its own first row (causal:
+    key j <= query i within the sequence). Returns o [T, H, d] and lse [H, T]. The definition of
+    "Attention from first principles" is applied to each sequence on its own, the way SURVEY's
+    next step f1 (ragged batches by per-sequence offsets) reads the grouped prefill.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    T, H, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (T, H_kv, d) or v.shape != k.shape or H % H_kv != 0:
+        raise ValueError("expected q [T,H,d], k/v [T,H_kv,d] with H % H_kv == 0")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, end at T and not decrease")
+    g = H // H_kv
+    o = np.zeros((T, H, d))
+    lse = np.zeros((H, T))
+    for b in range(len(cu) - 1):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        if r1 == r0:
+            continue
+        for h in range(H):
+            hk = h // g
+            s = _scores(q[r0:r1, h], k[r0:r1, hk], causal, scale)
+            p, lse[h, r0:r1] = _softmax_rows(s)
+            o[r0:r1, h] = p @ v[r0:r1, hk]
+    return o, lse
+
+
+def attention_fwd_varlen_rows(q, k, v, cu_seqlens, causal: bool, scale: float, rows):
+    """O and LSE of selected (token, head) rows of the ragged prefill, each from its own score row.
+
+    rows: integer array [n, 2] of (t, h). Returns (o [n, d], lse [n]).
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    H, H_kv, d = q.shape[1], k.shape[1], q.shape[2]
+    g = H // H_kv
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    o = np.empty((len(rows), d))
+    lse = np.empty(len(rows))
+    for r, (t, h) in enumerate(rows):
+        b = int(np.searchsorted(cu, t, side="right")) - 1  # cu[b] <= t < cu[b+1]
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        hk = h // g
+        k_end = t + 1 if causal else r1  # causal row t sees the sequence's rows r0 .. t
+        s = scale * (k[r0:k_end, hk] @ q[t, h])
+        p, lse_r = _softmax_rows(s[None, :])
+        o[r] = p[0] @ v[r0:k_end, hk]
         lse[r] = lse_r[0]
     return o, lse
 

@@ -31,6 +31,9 @@ MUTANTS = {
     "bwd_dk_no_scale": ("dk[b, hk] += scale * (ds.T @ q[b, h])", "dk[b, hk] += (ds.T @ q[b, h])"),
     "bwd_dv_transposed": ("dv[b, hk] += p.T @ dout[b, h]", "dv[b, hk] += p @ dout[b, h]"),
     "rows_causal_off_by_one": ("n_keys = i + 1 if causal else N", "n_keys = i if causal else N"),
+    "varlen_crosses_sequences": ("s = _scores(q[r0:r1, h], k[r0:r1, hk], causal, scale)",
+                                 "s = _scores(q[r0:r1, h], k[:r1, hk], causal, scale)"),
+    "varlen_rows_global_causal": ("k_end = t + 1 if causal else r1", "k_end = t + 1 - r0 if causal else r1"),
     "decode_reads_one_short": ("kh = np.asarray(k_cache[b, hk, :n], dtype=np.float64)",
                                "kh = np.asarray(k_cache[b, hk, :n - 1], dtype=np.float64)"),
 }
@@ -54,6 +57,8 @@ PIN_CALLS = [
     (pins.test_bwd_sum_invariants, dict(causal=True)),
     (pins.test_bwd_constant_v_and_zero_scale, {}),
     (pins.test_bwd_causal_last_key, {}),
+    (pins.test_varlen_equals_block_diagonal_mask, dict(causal=True, H=4, H_kv=2)),
+    (pins.test_varlen_rows_agree_with_full, dict(causal=True)),
 ]
 
 

@@ -283,3 +283,70 @@ def test_bwd_causal_last_key():
     # only the last query sees the last key: dV_{N-1} = p_{N-1,N-1} dO_{N-1}
     p_last = math.exp(scale * float(q[0, 0, -1] @ k[0, 0, -1]) - lse[0, 0, -1])
     np.testing.assert_allclose(dv[0, 0, -1], p_last * do[0, 0, -1], atol=1e-14)
+
+
+# ------------------------------------------------------- ragged prefill ---
+
+def packed(lengths, H, H_kv, d):
+    T = int(sum(lengths))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return rand(T, H, d), rand(T, H_kv, d), rand(T, H_kv, d), cu
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 2), (4, 1)])
+def test_varlen_equals_block_diagonal_mask(causal, H, H_kv):
+    # A different formulation: one attention over all T packed rows whose mask allows exactly the
+    # pairs inside one sequence (and j <= i within it when causal), via torch SDPA in float64.
+    lengths = [5, 1, 0, 12, 7]
+    q, k, v, cu = packed(lengths, H, H_kv, 8)
+    scale = 0.35
+    o, lse = orc.attention_fwd_varlen(q, k, v, cu, causal, scale)
+    T = q.shape[0]
+    seq = np.repeat(np.arange(len(lengths)), lengths)
+    pos = np.arange(T)
+    allow = seq[:, None] == seq[None, :]
+    if causal:
+        allow &= pos[None, :] <= pos[:, None]
+    g = H // H_kv
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None].repeat_interleave(g, dim=1)
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None].repeat_interleave(g, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(allow),
+                                                           scale=scale)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+    s = scale * (qt @ kt.transpose(-1, -2))
+    ref_lse = torch.logsumexp(s.masked_fill(~torch.from_numpy(allow), float("-inf")), dim=-1)[0].numpy()
+    np.testing.assert_allclose(lse, ref_lse, atol=1e-12)
+
+
+def test_varlen_single_sequence_is_dense():
+    q, k, v, cu = packed([19], 4, 2, 8)
+    o, lse = orc.attention_fwd_varlen(q, k, v, cu, True, 0.5)
+    od, ld = orc.attention_fwd(q.transpose(1, 0, 2)[None], k.transpose(1, 0, 2)[None],
+                               v.transpose(1, 0, 2)[None], True, 0.5)
+    np.testing.assert_allclose(o, od[0].transpose(1, 0, 2), atol=1e-13)
+    np.testing.assert_allclose(lse, ld[0], atol=1e-13)
+
+
+def test_varlen_sequence_order_does_not_matter():
+    lengths = [6, 9, 3]
+    q, k, v, cu = packed(lengths, 2, 2, 4)
+    o, lse = orc.attention_fwd_varlen(q, k, v, cu, True, 0.8)
+    order = [2, 0, 1]
+    idx = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in order])
+    cu2 = np.concatenate([[0], np.cumsum([lengths[b] for b in order])])
+    o2, lse2 = orc.attention_fwd_varlen(q[idx], k[idx], v[idx], cu2, True, 0.8)
+    np.testing.assert_allclose(o2, o[idx], atol=1e-13)
+    np.testing.assert_allclose(lse2, lse[:, idx], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_rows_agree_with_full(causal):
+    q, k, v, cu = packed([4, 11, 1, 7], 4, 2, 8)
+    o, lse = orc.attention_fwd_varlen(q, k, v, cu, causal, 0.3)
+    rows = np.array([(0, 0), (3, 1), (4, 3), (14, 2), (15, 0), (22, 3), (16, 1)])
+    ro, rl = orc.attention_fwd_varlen_rows(q, k, v, cu, causal, 0.3, rows)
+    np.testing.assert_allclose(ro, o[rows[:, 0], rows[:, 1]], atol=1e-13)
+    np.testing.assert_allclose(rl, lse[rows[:, 1], rows[:, 0]], atol=1e-13)
+
