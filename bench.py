@@ -243,7 +243,8 @@ def main():
 
 
 def run_legs(torch, lib, I, L, reps=20):
-    """Extra legs: the 4k prefill forward (causal and not), the 1k causal prefill, GQA decode."""
+    """Extra legs: the 4k prefill forward (causal and not), the 1k causal prefill, the ragged
+    prefill, GQA decode."""
     legs = {}
     for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
         w = I.WORKLOADS[name]
@@ -262,6 +263,29 @@ def run_legs(torch, lib, I, L, reps=20):
         log(f"[bench] leg {name}: {legs[name]['avg_ms']:.3f} ms, {legs[name]['tflops']:.1f} TFLOP/s")
         del t, o, lse
         torch.cuda.empty_cache()
+
+    w = I.WORKLOADS["prefill_varlen"]
+    t = I.make_varlen(w)
+    lengths = t["lengths"]
+    cu = t["cu_seqlens"].cuda()
+    t = {k: t[k].cuda() for k in ("q", "k", "v")}
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.H, t["q"].shape[0]), dtype=torch.float32, device="cuda")
+    max_len = int(lengths.max())
+    fn = lambda: lib.fwd_varlen(t["q"], t["k"], t["v"], cu, max_len, w.causal, w.scale, out=o, lse=lse)  # noqa
+    for _ in range(3):
+        fn()
+    wall, stats = time_region(torch, lib, fn, reps)
+    (kname, st), = stats.items()
+    fl = L.varlen_fwd_flops(w.H, w.d, lengths, w.causal)
+    legs["prefill_varlen"] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": fl / (st["avg_ms"] * 1e-3) / 1e12,
+                              "frac_of_peak": fl / (st["avg_ms"] * 1e-3) / 1e12 / L.PEAK_BF16_TFLOPS,
+                              "wall_ms_per_call": wall / reps * 1e3, "tokens": int(lengths.sum()),
+                              "sequences": int(len(lengths)), "max_len": max_len}
+    log(f"[bench] leg prefill_varlen: {st['avg_ms']:.3f} ms, {legs['prefill_varlen']['tflops']:.1f} TFLOP/s "
+        f"({int(lengths.sum())} tokens in {len(lengths)} sequences)")
+    del t, o, lse, cu
+    torch.cuda.empty_cache()
 
     w = I.WORKLOADS["decode_gqa"]
     t = I.make_decode(w)

@@ -72,6 +72,26 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int dtype, void* stream);
 
 /*
+ * Ragged (variable-length) prefill: B sequences of different lengths packed row after row, with
+ * no padding. A padded batch of ragged sequences runs partly empty ("Why Fast GPUs Still Wait for
+ * Memory", section "Shapes matter", trap "B* is not a batch size you can actually run"); here each
+ * workgroup covers query rows of one sequence only. Each sequence is computed exactly as attn_fwd
+ * computes one (batch) entry: it attends only to its own rows, and causal positions count from
+ * its first row.
+ *   q, o [T, H, d] bf16; k, v [T, H_kv, d] bf16 (row t of every head contiguous, d innermost);
+ *   lse [H, T] float32 natural log, or NULL; cu_seqlens [B + 1] int32 DEVICE array, sequence b is
+ *   rows cu_seqlens[b] .. cu_seqlens[b+1] - 1, with cu_seqlens[0] = 0, non-decreasing, and
+ *   cu_seqlens[B] = T. max_seqlen >= every sequence length (it sizes the grid). The kernel clamps
+ *   offsets into [0, T] and lengths to max_seqlen, so malformed offsets cannot make it access
+ *   memory outside the tensors, but the results are then unspecified; rows of an empty sequence
+ *   are simply absent. T == 0 returns ATTN_OK without device work.
+ * dtype must be ATTN_BF16; d in {64, 128}; H % H_kv == 0.
+ */
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int B, int max_seqlen, int T, int H, int H_kv, int d,
+                            int causal, float scale, int dtype, void* stream);
+
+/*
  * Decode: one query token per (sequence, head) against a KV cache, the regime of
  * "Why Fast GPUs Still Wait for Memory", section "Attention III - KV cache, GQA, MLA"
  * (I = 2g/s, memory-bound). The key range of each sequence is split across workgroups and a

@@ -31,6 +31,7 @@ SIGNATURES = {
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
@@ -117,6 +118,38 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, scale: 
         _need(lse, "lse", torch.float32, (B, H, N), q.device)
     _check(_lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, N, d, int(bool(causal)),
                          float(scale), _DTYPES[q.dtype], _stream(q.device)))
+    return out, lse
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+               causal: bool, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """Ragged prefill: q [T,H,d], k/v [T,H_kv,d] bf16 packed rows, cu_seqlens [B+1] int32 on the GPU.
+
+    Returns (o [T,H,d], lse [H,T])."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [T, H, d]")
+    T, H, d = q.shape
+    H_kv = k.shape[1]
+    _need(k, "k", torch.bfloat16, (T, H_kv, d), q.device)
+    _need(v, "v", torch.bfloat16, (T, H_kv, d), q.device)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, None, q.device)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with B + 1 >= 2 entries")
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (H, T), q.device)
+    _check(_lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), B,
+                                int(max_seqlen), T, H, H_kv, d, int(bool(causal)), float(scale), ATTN_BF16,
+                                _stream(q.device)))
     return out, lse
 
 

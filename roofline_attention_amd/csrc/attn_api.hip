@@ -130,7 +130,7 @@ TimedScope::~TimedScope() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -168,6 +168,35 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                                          static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, H_kv, N, d,
                                          causal != 0, scale, s));
   return hip_status(ra::launch_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0, scale, s));
+}
+
+
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens, int B, int max_seqlen, int T, int H, int H_kv, int d,
+                            int causal, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v, o and cu_seqlens must be non-null");
+  if (T < 0) return fail(ATTN_ERR_INVALID_ARG, "T must be >= 0");
+  attn_status st = check_shape(B, H, H_kv, max_seqlen, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "ragged prefill supports ATTN_BF16 only");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens and lse must be 4-byte aligned");
+  const size_t qb = (size_t)T * H * d * 2, kb = (size_t)T * H_kv * d * 2, lb = (size_t)H * T * 4;
+  const Range rq{q, qb}, rk{k, kb}, rv{v, kb}, ro{o, qb}, rl{lse, lse ? lb : 0}, rc{cu_seqlens, (size_t)(B + 1) * 4};
+  const Range outs[] = {ro, rl};
+  const Range ins[] = {rq, rk, rv, rc};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs overlap inputs");
+  if (overlap(ro, rl)) return fail(ATTN_ERR_INVALID_ARG, "o and lse overlap");
+  const long long tiles = (long long)((max_seqlen + 63) / 64) * H * B;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  if (T == 0) return ok();  // no rows
+  return hip_status(ra::launch_fwd_bf16_varlen(q, k, v, o, lse, cu_seqlens, B, max_seqlen, T, H, H_kv, d,
+                                               causal != 0, scale, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_decode_workspace_size(int B, int H, int N_cap, int d) {

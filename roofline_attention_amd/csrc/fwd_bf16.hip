@@ -64,11 +64,11 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int HD, bool CAUSAL>
+template <int HD, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int H, int group, int N, int n_qtiles,
-    float scale_log2) {
+    bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ cu_seqlens, int T, int H,
+    int group, int N, int n_qtiles, float scale_log2) {
   __shared__ FwdSmem<HD> sm;
   constexpr int KSTEPS = HD / 16;  // MFMA k-steps over the head dimension
   constexpr int CBLK = HD / 32;    // 32-wide head-dimension blocks of O^T
@@ -91,8 +91,29 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const size_t q_head = ((size_t)b * H + h) * (size_t)N * HD;
-  const size_t kv_head = ((size_t)b * Hkv + hk) * (size_t)N * HD;
+  // Rows of this (sequence, head): dense [B,H,N,d] / [B,H_kv,N,d] with N rows per sequence, or
+  // packed [T,H,d] / [T,H_kv,d] with sequence b at rows cu_seqlens[b] .. cu_seqlens[b+1] - 1 (N is
+  // then the longest length the grid covers). Offsets read from the device array are clamped into
+  // [0, T] and lengths to N, so no access leaves the tensors whatever they hold. Row strides and
+  // bases are in elements; LSE is [B,H,N] or [H,T].
+  int Nb = N;
+  size_t q_base, kv_base, lse_base;
+  int rs_q = HD, rs_kv = HD;
+  if constexpr (VARLEN) {
+    const int start = min(max(cu_seqlens[b], 0), T);
+    const int end = min(max(cu_seqlens[b + 1], start), T);
+    Nb = min(end - start, N);
+    q_base = ((size_t)start * H + h) * HD;
+    kv_base = ((size_t)start * Hkv + hk) * HD;
+    lse_base = (size_t)h * T + start;
+    rs_q = H * HD;
+    rs_kv = Hkv * HD;
+  } else {
+    q_base = ((size_t)b * H + h) * (size_t)N * HD;
+    kv_base = ((size_t)b * Hkv + hk) * (size_t)N * HD;
+    lse_base = ((size_t)b * H + h) * N;
+  }
+  if (qt * FWD_BR >= Nb) return;  // query tile past this sequence (uniform, before any barrier)
   const int q0 = qt * FWD_BR + w * 32;
   const int qi = q0 + l32;
 
@@ -103,8 +124,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   const bool neg = scale_log2 < 0.f;
   const float c = fmaxf(neg ? -scale_log2 : scale_log2, FLT_MIN);
   bf16x8 qf[KSTEPS];
-  if (qi < N) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + q_head + (size_t)qi * HD);
+  if (qi < Nb) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + q_base + (size_t)qi * rs_q);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       qf[kk] = src[2 * kk + g];
@@ -115,30 +136,32 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = bf16x8{};
   }
 
-  const int q_end = min(N, qt * FWD_BR + FWD_BR);
-  const int n_kt = CAUSAL ? (q_end + FWD_BC - 1) / FWD_BC : (N + FWD_BC - 1) / FWD_BC;
+  const int q_end = min(Nb, qt * FWD_BR + FWD_BR);
+  const int n_kt = CAUSAL ? (q_end + FWD_BC - 1) / FWD_BC : (Nb + FWD_BC - 1) / FWD_BC;
 
   // Direct-to-LDS staging: wave w issues blocks w, w + 4, ... of a tile (RPI rows each). Lane i
   // fills row blk*RPI + i / CHUNKS at chunk position i % CHUNKS with global chunk
   // position ^ swz(row). The swizzles repeat within 4*RPI rows, so a lane's byte offset moves by
   // BLK_BYTES from one of its blocks to the next. The buffer resource of tile kt starts at its
-  // first row and ends at the sequence end, so rows past N load as zeros.
-  constexpr int BLK_BYTES = 4 * RPI * HD * 2;  // byte distance between this wave's blocks
+  // first row and ends with the last byte of the tile's last row inside the sequence, so rows past
+  // the sequence end load as zeros.
+  const int BLK_BYTES = 4 * RPI * rs_kv * 2;  // byte distance between this wave's blocks
   const int st_row = w * RPI + lane / CHUNKS;
-  const int k_voff = (st_row * HD + (((lane % CHUNKS) ^ swz_k<HD>(st_row)) * 8)) * 2;
-  const int v_voff = (st_row * HD + (((lane % CHUNKS) ^ swz_v<HD>(st_row)) * 8)) * 2;
-  const bf16* k_head = K + kv_head;
-  const bf16* v_head = V + kv_head;
+  const int k_voff = (st_row * rs_kv + (((lane % CHUNKS) ^ swz_k<HD>(st_row)) * 8)) * 2;
+  const int v_voff = (st_row * rs_kv + (((lane % CHUNKS) ^ swz_v<HD>(st_row)) * 8)) * 2;
+  const bf16* k_head = K + kv_base;
+  const bf16* v_head = V + kv_base;
+  auto tile_bytes = [&](int row0) { return (min(Nb - row0, FWD_BC) - 1) * rs_kv * 2 + HD * 2; };
   auto issue_k = [&](int kt, int stage) {
     const int row0 = kt * FWD_BC;
-    const u32x4 rsrc = dma_rsrc(k_head + (size_t)row0 * HD, (N - row0) * HD * 2);
+    const u32x4 rsrc = dma_rsrc(k_head + (size_t)row0 * rs_kv, tile_bytes(row0));
 #pragma unroll
     for (int u = 0; u < BLOCKS / 4; ++u)
       load_to_lds<16>(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * 4 + w) * RPI * HD]);
   };
   auto issue_v = [&](int kt, int stage) {
     const int row0 = kt * FWD_BC;
-    const u32x4 rsrc = dma_rsrc(v_head + (size_t)row0 * HD, (N - row0) * HD * 2);
+    const u32x4 rsrc = dma_rsrc(v_head + (size_t)row0 * rs_kv, tile_bytes(row0));
 #pragma unroll
     for (int u = 0; u < BLOCKS / 4; ++u)
       load_to_lds<16>(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * 4 + w) * RPI * HD]);
@@ -182,7 +205,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+        if (key >= Nb || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
       }
     }
   };
@@ -246,7 +269,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
 
   auto is_boundary = [&](int kt) {
     const int k0 = kt * FWD_BC;
-    return (k0 + FWD_BC > N) || (CAUSAL && k0 + FWD_BC - 1 > q0);
+    return (k0 + FWD_BC > Nb) || (CAUSAL && k0 + FWD_BC - 1 > q0);
   };
 
   // Prologue: K0, V0 and K1 in flight, then S^T of tile 0.
@@ -304,9 +327,9 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
   }
 
   l_run += __shfl_xor(l_run, 32, 64);
-  if (qi < N) {
+  if (qi < Nb) {
     const float inv = 1.f / l_run;
-    bf16* orow = O + q_head + (size_t)qi * HD;
+    bf16* orow = O + q_base + (size_t)qi * rs_q;
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) {
 #pragma unroll
@@ -316,20 +339,20 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
         *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * rg + 4 * g) = t;
       }
     }
-    if (LSE != nullptr && g == 0) LSE[((size_t)b * H + h) * N + qi] = (m_run + log2f(l_run)) * kLn2;
+    if (LSE != nullptr && g == 0) LSE[lse_base + qi] = (m_run + log2f(l_run)) * kLn2;
   }
 }
 
-template <int HD, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                  int H_kv, int N, float scale, hipStream_t stream, const char* name) {
+template <int HD, bool CAUSAL, bool VARLEN>
+hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens, int T,
+                  int B, int H, int H_kv, int N, float scale, hipStream_t stream, const char* name) {
   const int n_qt = (N + FWD_BR - 1) / FWD_BR;
   const long long total = (long long)n_qt * H * B;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   TimedScope ts(name, stream);
-  hipLaunchKernelGGL((fwd_bf16_kernel<HD, CAUSAL>), dim3((unsigned)total), dim3(FWD_THREADS), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<HD, CAUSAL, VARLEN>), dim3((unsigned)total), dim3(FWD_THREADS), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<bf16*>(o), lse, H, H / H_kv, N, n_qt, scale * kLog2e);
+                     static_cast<bf16*>(o), lse, cu_seqlens, T, H, H / H_kv, N, n_qt, scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -338,11 +361,29 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int H_kv, int N, int d, bool causal, float scale, hipStream_t stream) {
   if (d == 128) {
-    return causal ? launch<128, true>(q, k, v, o, lse, B, H, H_kv, N, scale, stream, "fwd_bf16_d128_causal")
-                  : launch<128, false>(q, k, v, o, lse, B, H, H_kv, N, scale, stream, "fwd_bf16_d128");
+    return causal ? launch<128, true, false>(q, k, v, o, lse, nullptr, 0, B, H, H_kv, N, scale, stream,
+                                             "fwd_bf16_d128_causal")
+                  : launch<128, false, false>(q, k, v, o, lse, nullptr, 0, B, H, H_kv, N, scale, stream,
+                                              "fwd_bf16_d128");
   }
-  return causal ? launch<64, true>(q, k, v, o, lse, B, H, H_kv, N, scale, stream, "fwd_bf16_d64_causal")
-                : launch<64, false>(q, k, v, o, lse, B, H, H_kv, N, scale, stream, "fwd_bf16_d64");
+  return causal ? launch<64, true, false>(q, k, v, o, lse, nullptr, 0, B, H, H_kv, N, scale, stream,
+                                          "fwd_bf16_d64_causal")
+                : launch<64, false, false>(q, k, v, o, lse, nullptr, 0, B, H, H_kv, N, scale, stream, "fwd_bf16_d64");
+}
+
+hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const int32_t* cu_seqlens, int B, int max_seqlen, int T, int H, int H_kv, int d,
+                                  bool causal, float scale, hipStream_t stream) {
+  if (d == 128) {
+    return causal ? launch<128, true, true>(q, k, v, o, lse, cu_seqlens, T, B, H, H_kv, max_seqlen, scale, stream,
+                                            "fwd_bf16_varlen_d128_causal")
+                  : launch<128, false, true>(q, k, v, o, lse, cu_seqlens, T, B, H, H_kv, max_seqlen, scale, stream,
+                                             "fwd_bf16_varlen_d128");
+  }
+  return causal ? launch<64, true, true>(q, k, v, o, lse, cu_seqlens, T, B, H, H_kv, max_seqlen, scale, stream,
+                                         "fwd_bf16_varlen_d64_causal")
+                : launch<64, false, true>(q, k, v, o, lse, cu_seqlens, T, B, H, H_kv, max_seqlen, scale, stream,
+                                          "fwd_bf16_varlen_d64");
 }
 
 }  // namespace ra

@@ -27,6 +27,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int H_kv, int N, int d, bool causal, float scale,
                            hipStream_t stream);
 
+// Ragged prefill over packed rows: q, o [T,H,d], k, v [T,H_kv,d], lse [H,T]; sequence b is rows
+// cu_seqlens[b] .. cu_seqlens[b+1] - 1 (device array), each at most max_seqlen long.
+hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const int32_t* cu_seqlens, int B, int max_seqlen, int T, int H, int H_kv, int d,
+                                  bool causal, float scale, hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int B, int H, int H_kv, int N, int d, bool causal, float scale,
                           hipStream_t stream);

@@ -18,7 +18,9 @@ Recipe (the pages fix none of it; the workloads are synthetic sweeps shaped like
 * bf16 storage uses round-to-nearest-even (torch's float32 -> bfloat16 cast);
 * decode KV lengths are integers drawn inclusively from [lo, hi]; cache rows at
   or beyond a sequence's length are filled with NaN so that any read of them
-  shows up in the result.
+  shows up in the result;
+* a ragged prefill batch draws its lengths from the same length stream and packs
+  the (b, h) blocks of each tensor row after row ([T, H, d], offsets cu_seqlens).
 """
 from __future__ import annotations
 
@@ -58,7 +60,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the headline metric, in order.
+# The workloads of the headline metric, then the ragged prefill.
 WORKLOADS = {
     "tiny_f32": Workload("tiny_f32", "fwd", 1, 2, 2, 128, 64, "f32", False, seed=1),
     "prefill_causal_1k": Workload("prefill_causal_1k", "fwd", 4, 16, 16, 1024, 64, "bf16", True, seed=2),
@@ -68,6 +70,10 @@ WORKLOADS = {
     "decode_gqa": Workload("decode_gqa", "decode", 64, 32, 8, 8192, 128, "bf16", False, seed=4,
                            kv_lo=512, kv_hi=8192),
     "fwdbwd_4k_causal": Workload("fwdbwd_4k_causal", "fwdbwd", 2, 16, 16, 4096, 128, "bf16", True, seed=5),
+    # Ragged prefill (packed rows, per-sequence offsets): 16 sequences with the decode length mix,
+    # grouped heads 32/8; N is the longest length the grid must cover.
+    "prefill_varlen": Workload("prefill_varlen", "varlen", 16, 32, 8, 8192, 128, "bf16", True, seed=6,
+                               kv_lo=512, kv_hi=8192),
 }
 
 
@@ -112,6 +118,33 @@ def make_prefill(w: Workload, with_dout: Optional[bool] = None) -> dict:
     if with_dout:
         t["do"] = make_tensor(w.seed, TENSOR_DO, w.B, w.H, w.N, w.d, w.dtype)
     return t
+
+
+def make_varlen(w: Workload, lengths=None) -> dict:
+    """Packed ragged batch: q [T,H,d], k/v [T,H_kv,d], cu_seqlens [B+1] int32, lengths [B].
+
+    Lengths come from the kv-length stream (inclusive [kv_lo, kv_hi]) unless given; the rows of
+    sequence b and head h are the (b, h) block of each tensor's streams, placed at rows
+    cu_seqlens[b] .. cu_seqlens[b+1] - 1.
+    """
+    if lengths is None:
+        lengths = kv_lengths(w.seed, w.B, w.kv_lo, w.kv_hi)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    dt = torch_dtype(w.dtype)
+    out = {}
+    for name, tid, heads, factor in (("q", TENSOR_Q, w.H, w.qk_factor), ("k", TENSOR_K, w.H_kv, w.qk_factor),
+                                     ("v", TENSOR_V, w.H_kv, 1.0)):
+        t = torch.empty((T, heads, w.d), dtype=dt)
+        for b in range(len(lengths)):
+            for h in range(heads):
+                blk = normal_block(w.seed, tid, b, h, (int(lengths[b]), w.d), factor)
+                t[cu[b]:cu[b + 1], h].copy_(torch.from_numpy(blk))
+        out[name] = t
+    out["cu_seqlens"] = torch.from_numpy(cu)
+    out["lengths"] = lengths
+    return out
 
 
 def make_decode(w: Workload, nan_pad: bool = True) -> dict:

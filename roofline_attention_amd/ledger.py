@@ -28,6 +28,11 @@ def fwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     return w / 2 if causal else w
 
 
+def varlen_fwd_flops(H: int, d: int, lengths, causal: bool) -> float:
+    """Algorithmic forward FLOPs of a ragged batch: each sequence counts as its own dense case."""
+    return sum(fwd_flops(1, H, int(n), d, causal) for n in lengths)
+
+
 def bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     return 2.5 * fwd_flops(B, H, N, d, causal)
 

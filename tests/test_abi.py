@@ -41,7 +41,7 @@ def test_binding_signatures_cover_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     assert lib.attn_status_string(OK) == b"ATTN_OK"
     assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
     assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
@@ -84,6 +84,25 @@ def test_fwd_rejects_null_misaligned_and_overlapping(lib):
     ov = list(p)
     ov[4] = ctypes.c_void_p(BASE + 3 * GAP + 16)  # lse inside o
     assert fwd(lib, ptrs=ov) == INVALID
+
+
+def test_fwd_varlen_validation(lib):
+    p = [addr(i) for i in range(6)]
+
+    def call(B=3, max_seqlen=100, T=250, H=4, H_kv=2, d=128, dtype=BF16, cu=p[5], lse=p[4]):
+        return lib.attn_fwd_varlen(p[0], p[1], p[2], p[3], lse, cu, B, max_seqlen, T, H, H_kv, d, 1, 0.088, dtype,
+                                   None)
+
+    assert call(cu=None) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(B=0) == INVALID
+    assert call(max_seqlen=0) == INVALID
+    assert call(H=4, H_kv=3) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(cu=ctypes.c_void_p(BASE + 5 * GAP + 2)) == INVALID  # misaligned offsets
+    assert call(lse=ctypes.c_void_p(BASE + 3 * GAP + 64)) == INVALID  # lse inside o
+    assert call(T=0) == OK  # no rows: nothing is launched
 
 
 def test_decode_validation(lib):

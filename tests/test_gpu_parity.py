@@ -142,6 +142,67 @@ def test_forward_is_deterministic(lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+# --------------------------------------------------------------------- ragged prefill ----
+
+def varlen_case(lib, w, lengths=None):
+    t = I.make_varlen(w, lengths)
+    o, lse = lib.fwd_varlen(dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["cu_seqlens"]), int(max(t["lengths"].max(), 1)),
+                            w.causal, w.scale)
+    torch.cuda.synchronize()
+    return t, o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv,d", [(4, 2, 128), (4, 4, 64), (8, 1, 128)])
+def test_fwd_varlen_ragged_lengths(lib, H, H_kv, d, causal):
+    w = I.Workload("vl", "varlen", 5, H, H_kv, 600, d, "bf16", causal, seed=21)
+    t, o, lse = varlen_case(lib, w, lengths=[1, 255, 256, 257, 600])
+    ro, rl = orc.attention_fwd_varlen(f64(t["q"]), f64(t["k"]), f64(t["v"]), t["cu_seqlens"].numpy(), causal,
+                                      w.scale)
+    assert max_err(o, ro) <= TOL_BF16
+    assert max_err(lse, rl) <= TOL_BF16
+
+
+def test_fwd_varlen_empty_sequences(lib):
+    w = I.Workload("vl0", "varlen", 4, 2, 2, 700, 128, "bf16", True, seed=22)
+    t, o, lse = varlen_case(lib, w, lengths=[0, 700, 0, 3])
+    ro, rl = orc.attention_fwd_varlen(f64(t["q"]), f64(t["k"]), f64(t["v"]), t["cu_seqlens"].numpy(), True, w.scale)
+    assert max_err(o, ro) <= TOL_BF16 and max_err(lse, rl) <= TOL_BF16
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_varlen_equal_lengths_match_dense_bitwise(lib, causal):
+    # Same sequences through both layouts: the kernel does the same arithmetic, only the row
+    # strides differ, so the outputs must be identical.
+    B, H, H_kv, N, d = 3, 4, 2, 333, 128
+    w = I.Workload("vld", "varlen", B, H, H_kv, N, d, "bf16", causal, seed=23)
+    t, o, lse = varlen_case(lib, w, lengths=[N] * B)
+    q = t["q"].view(B, N, H, d).permute(0, 2, 1, 3).contiguous()
+    k = t["k"].view(B, N, H_kv, d).permute(0, 2, 1, 3).contiguous()
+    v = t["v"].view(B, N, H_kv, d).permute(0, 2, 1, 3).contiguous()
+    od, ld = lib.fwd(dev(q), dev(k), dev(v), causal, w.scale)
+    assert torch.equal(o.view(B, N, H, d).permute(0, 2, 1, 3), od.cpu())
+    assert torch.equal(lse.view(H, B, N).permute(1, 0, 2), ld.cpu())
+
+
+def test_fwd_varlen_full_workload_sampled_rows(lib):
+    w = I.WORKLOADS["prefill_varlen"]
+    t, o, lse = varlen_case(lib, w)
+    cu = t["cu_seqlens"].numpy()
+    rng = np.random.default_rng(7)
+    rows = []
+    for b in range(w.B):  # first, last and two random rows of every sequence, random heads
+        for i in (0, int(t["lengths"][b]) - 1, *rng.integers(0, t["lengths"][b], 2)):
+            rows.append((int(cu[b]) + int(i), int(rng.integers(0, w.H))))
+    rows = np.array(rows)
+    ro, rl = orc.attention_fwd_varlen_rows(f64(t["q"]), f64(t["k"]), f64(t["v"]), cu, w.causal, w.scale, rows)
+    eo = float(np.max(np.abs(f64(o[rows[:, 0], rows[:, 1]]) - ro)))
+    el = float(np.max(np.abs(f64(lse[rows[:, 1], rows[:, 0]]) - rl)))
+    print(f"prefill_varlen: {len(rows)} rows, max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_BF16 and el <= TOL_BF16
+    assert torch.isfinite(o.float()).all()
+
+
 # ----------------------------------------------------------------------------- decode ----
 
 def decode_check(lib, w, kv_len=None, n_seq_check=None):
