@@ -21,7 +21,8 @@ design notes):
   * grouped-query attention maps query head h to KV head h // (H / H_kv)
     (section "Attention III - KV cache, GQA, MLA" gives only g = h / h_kv);
   * LSE is the natural-log log-sum-exp of each score row over unmasked keys;
-  * decode is one query row against the first kv_len[b] cache rows;
+  * decode is one query row against the first kv_len[b] cache rows; a paged cache
+    maps logical row j to row j % page_size of page block_table[b, j // page_size];
   * a ragged (variable-length) batch packs its sequences' rows one after another
     ([T, H, d], offsets cu_seqlens); each sequence attends only within itself, and a
     causal position is counted from the sequence's first row;
@@ -187,6 +188,39 @@ def attention_decode(q, k_cache, v_cache, kv_len, scale: float):
             s = scale * (kh @ q[b, h])
             p, lse_r = _softmax_rows(s[None, :])
             o[b, h] = p[0] @ vh
+            lse[b, h] = lse_r[0]
+    return o, lse
+
+
+def attention_decode_paged(q, k_pages, v_pages, block_table, kv_len, scale: float):
+    """Decode over a paged KV cache.
+
+    k_pages/v_pages [P, H_kv, page_size, d] hold the cache in fixed-size pages; logical cache row j
+    of sequence b is row j % page_size of physical page block_table[b, j // page_size]. The pages
+    of a sequence need not be contiguous or in order ("M4.2 - GPU Execution Model for Transformer
+    Kernels", section 0x0D, failure 16: logical K/V continuity does not imply contiguous physical
+    addresses). The logical rows are gathered, then the plain decode definition applies.
+    Returns (o [B,H,d], lse [B,H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, d = q.shape
+    P, H_kv, ps, _ = k_pages.shape
+    g = H // H_kv
+    table = np.asarray(block_table, dtype=np.int64)
+    o = np.empty((B, H, d))
+    lse = np.empty((B, H))
+    for b in range(B):
+        n = int(kv_len[b])
+        if not 1 <= n <= table.shape[1] * ps:
+            raise ValueError("kv_len out of range")
+        pages = table[b, :(n + ps - 1) // ps]
+        for h in range(H):
+            hk = h // g
+            kh = np.concatenate([np.asarray(k_pages[p, hk], dtype=np.float64) for p in pages])[:n]
+            vh = np.concatenate([np.asarray(v_pages[p, hk], dtype=np.float64) for p in pages])[:n]
+            s = scale * (kh @ q[b, h])
+            pr, lse_r = _softmax_rows(s[None, :])
+            o[b, h] = pr[0] @ vh
             lse[b, h] = lse_r[0]
     return o, lse
 

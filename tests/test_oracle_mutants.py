@@ -34,6 +34,9 @@ MUTANTS = {
     "varlen_crosses_sequences": ("s = _scores(q[r0:r1, h], k[r0:r1, hk], causal, scale)",
                                  "s = _scores(q[r0:r1, h], k[:r1, hk], causal, scale)"),
     "varlen_rows_global_causal": ("k_end = t + 1 if causal else r1", "k_end = t + 1 - r0 if causal else r1"),
+    "paged_wrong_page": ("pages = table[b, :(n + ps - 1) // ps]", "pages = table[b, 1:(n + ps - 1) // ps + 1]"),
+    "paged_reads_first_head": ("np.asarray(k_pages[p, hk], dtype=np.float64) for p in pages",
+                               "np.asarray(k_pages[p, 0], dtype=np.float64) for p in pages"),
     "decode_reads_one_short": ("kh = np.asarray(k_cache[b, hk, :n], dtype=np.float64)",
                                "kh = np.asarray(k_cache[b, hk, :n - 1], dtype=np.float64)"),
 }
@@ -59,6 +62,8 @@ PIN_CALLS = [
     (pins.test_bwd_causal_last_key, {}),
     (pins.test_varlen_equals_block_diagonal_mask, dict(causal=True, H=4, H_kv=2)),
     (pins.test_varlen_rows_agree_with_full, dict(causal=True)),
+    (pins.test_decode_paged_equals_contiguous, dict(shuffle=True)),
+    (pins.test_decode_paged_matches_sdpa, {}),
 ]
 
 

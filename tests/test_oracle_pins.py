@@ -204,6 +204,58 @@ def test_decode_is_last_causal_row():
     np.testing.assert_allclose(lsed, lse[:, :, -1], atol=1e-13)
 
 
+def to_pages(kc, page_size, order):
+    """Cut a contiguous cache [B,H_kv,N_cap,d] into pages [P,H_kv,ps,d] placed at `order`."""
+    B, H_kv, N_cap, d = kc.shape
+    per = N_cap // page_size
+    pages = np.full((B * per, H_kv, page_size, d), np.nan)
+    table = np.empty((B, per), dtype=np.int64)
+    for b in range(B):
+        for j in range(per):
+            phys = order[b * per + j]
+            pages[phys] = kc[b, :, j * page_size:(j + 1) * page_size]
+            table[b, j] = phys
+    return pages, table
+
+
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_decode_paged_equals_contiguous(shuffle):
+    # In-order pages of a contiguous cache, or the same pages scattered in physical memory, give
+    # the dense decode's result; unused pages and the unused tail of a last page are NaN.
+    B, H, H_kv, N_cap, d, ps = 3, 8, 2, 48, 8, 16
+    q = rand(B, H, d)
+    kc, vc = rand(B, H_kv, N_cap, d), rand(B, H_kv, N_cap, d)
+    kv_len = np.array([1, 17, 48])
+    for b in range(B):
+        kc[b, :, kv_len[b]:] = np.nan
+        vc[b, :, kv_len[b]:] = np.nan
+    order = RNG.permutation(B * N_cap // ps) if shuffle else np.arange(B * N_cap // ps)
+    kp, table = to_pages(kc, ps, order)
+    vp, _ = to_pages(vc, ps, order)
+    kp = np.concatenate([kp, np.full((2, H_kv, ps, d), np.nan)])  # pages no sequence references
+    vp = np.concatenate([vp, np.full((2, H_kv, ps, d), np.nan)])
+    o, lse = orc.attention_decode_paged(q, kp, vp, table, kv_len, 0.3)
+    od, lsed = orc.attention_decode(q, kc, vc, kv_len, 0.3)
+    np.testing.assert_array_equal(o, od)
+    np.testing.assert_array_equal(lse, lsed)
+
+
+def test_decode_paged_matches_sdpa():
+    B, H, H_kv, d, ps = 2, 4, 1, 8, 4
+    kp, vp = rand(7, H_kv, ps, d), rand(7, H_kv, ps, d)
+    table = np.array([[5, 0, 3], [6, 2, 1]])
+    kv_len = np.array([10, 12])
+    q = rand(B, H, d)
+    o, _ = orc.attention_decode_paged(q, kp, vp, table, kv_len, 0.5)
+    for b in range(B):
+        kb = torch.from_numpy(kp[table[b]].transpose(1, 0, 2, 3).reshape(H_kv, -1, d)[:, :kv_len[b]])
+        vb = torch.from_numpy(vp[table[b]].transpose(1, 0, 2, 3).reshape(H_kv, -1, d)[:, :kv_len[b]])
+        qb = torch.from_numpy(q[b])[:, None, :]
+        want = torch.nn.functional.scaled_dot_product_attention(qb, kb.expand(H, -1, -1), vb.expand(H, -1, -1),
+                                                                scale=0.5)[:, 0].numpy()
+        np.testing.assert_allclose(o[b], want, atol=1e-12)
+
+
 # --------------------------------------------------------------- backward ---
 
 def torch_grads(q, k, v, dout, causal, scale):
