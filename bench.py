@@ -244,7 +244,7 @@ def main():
 
 def run_legs(torch, lib, I, L, reps=20):
     """Extra legs: the 4k prefill forward (causal and not), the 1k causal prefill, the ragged
-    prefill, GQA decode."""
+    prefill, GQA decode over a contiguous and over a paged cache."""
     legs = {}
     for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
         w = I.WORKLOADS[name]
@@ -288,43 +288,56 @@ def run_legs(torch, lib, I, L, reps=20):
     torch.cuda.empty_cache()
 
     w = I.WORKLOADS["decode_gqa"]
-    t = I.make_decode(w)
-    lens = t["kv_len"].numpy().tolist()
-    t = {k: x.cuda() for k, x in t.items()}
-    o = torch.empty_like(t["q"])
-    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
-    wsd = torch.empty(lib.decode_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+    dense = I.make_decode(w)
+    lens = dense["kv_len"].numpy().tolist()
+    nbytes = L.decode_bytes(w.H, w.H_kv, w.d, 2, lens)
     # Read (not written) before each call to evict the cache: a written buffer would leave dirty
     # lines whose write-back then lands inside the timed kernel.
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB, above the 256 MB last-level cache
-    fn = lambda: lib.decode(t["q"], t["k"], t["v"], t["kv_len"], w.scale, out=o, lse=lse, workspace=wsd)  # noqa
-    for _ in range(3):
-        fn()
-    # cold: the cache flush runs outside the timed kernels
-    lib.timing_reset()
-    lib.timing_enable(True)
-    for _ in range(reps):
-        lib.timing_enable(False)
-        flush.sum()
+    o = torch.empty((w.B, w.H, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(lib.decode_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+
+    def cold_decode(fn, name, split_prefix, extra):
+        for _ in range(3):
+            fn()
+        # cold: the cache flush runs outside the timed kernels
+        lib.timing_reset()
         lib.timing_enable(True)
-        fn()
-    torch.cuda.synchronize()
-    lib.timing_enable(False)
-    stats = kernel_stats(lib)
-    lib.timing_reset()
-    nbytes = L.decode_bytes(w.H, w.H_kv, w.d, 2, lens)
-    total_ms = sum(s["avg_ms"] for s in stats.values())
-    split = [n for n in stats if n.startswith("decode_split")][0]
-    legs["decode_gqa"] = {
-        "kernels": {n: s["avg_ms"] for n, s in stats.items()},
-        "compulsory_bytes": nbytes,
-        "gbs_split_kernel": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9,
-        "gbs_both_kernels": nbytes / (total_ms * 1e-3) / 1e9,
-        "frac_of_peak_split": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9 / L.PEAK_HBM_GBS,
-        "cache": "cold (1 GiB buffer read before each call, outside the timed kernels)",
-        "tflops": L.decode_flops(w.H, w.d, lens) / (total_ms * 1e-3) / 1e12,
-    }
-    log(f"[bench] leg decode_gqa: {total_ms:.3f} ms, {legs['decode_gqa']['gbs_both_kernels']:.0f} GB/s")
+        for _ in range(reps):
+            lib.timing_enable(False)
+            flush.sum()
+            lib.timing_enable(True)
+            fn()
+        torch.cuda.synchronize()
+        lib.timing_enable(False)
+        stats = kernel_stats(lib)
+        lib.timing_reset()
+        total_ms = sum(s["avg_ms"] for s in stats.values())
+        split = [n for n in stats if n.startswith(split_prefix)][0]
+        legs[name] = {
+            "kernels": {n: s["avg_ms"] for n, s in stats.items()},
+            "compulsory_bytes": nbytes,
+            "gbs_split_kernel": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9,
+            "gbs_both_kernels": nbytes / (total_ms * 1e-3) / 1e9,
+            "frac_of_peak_split": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9 / L.PEAK_HBM_GBS,
+            "cache": "cold (1 GiB buffer read before each call, outside the timed kernels)",
+            "tflops": L.decode_flops(w.H, w.d, lens) / (total_ms * 1e-3) / 1e12,
+            **extra,
+        }
+        log(f"[bench] leg {name}: {total_ms:.3f} ms, {legs[name]['gbs_both_kernels']:.0f} GB/s")
+
+    t = {k: x.cuda() for k, x in dense.items()}
+    cold_decode(lambda: lib.decode(t["q"], t["k"], t["v"], t["kv_len"], w.scale, out=o, lse=lse, workspace=wsd),
+                "decode_gqa", "decode_split", {})
+    del t
+    paged = I.make_decode_paged(w, 64, dense=dense)
+    del dense
+    tp = {k: x.cuda() for k, x in paged.items()}
+    cold_decode(lambda: lib.decode_paged(tp["q"], tp["k_pages"], tp["v_pages"], tp["block_table"], tp["kv_len"],
+                                         w.scale, out=o, lse=lse, workspace=wsd),
+                "decode_gqa_paged", "decode_paged_split",
+                {"page_size": 64, "pages": int(paged["k_pages"].shape[0]), "placement": "seeded shuffle"})
     return legs
 
 

@@ -112,6 +112,27 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode over a paged KV cache: as attn_decode, but the cache lives in fixed-size pages that need
+ * not be contiguous or in order. A kernel's contract has to state the page layout when K/V is not
+ * contiguous ("M4.2 - GPU Execution Model for Transformer Kernels", section 0x06), and logical
+ * K/V continuity does not imply contiguous physical addresses (same page, section 0x0D, failure 16).
+ *   k_pages, v_pages [num_pages, H_kv, page_size, d] bf16: page p holds page_size consecutive cache
+ *   rows of every KV head, rows of one head contiguous. block_table [B, max_pages] int32 DEVICE
+ *   array: cache row j of sequence b is row j % page_size of page block_table[b][j / page_size].
+ *   kv_len [B] int32 DEVICE array, clamped to [0, max_pages * page_size] on the device; only
+ *   the table entries of rows below kv_len[b] are used. Page ids are clamped into [0, num_pages)
+ *   on the device, so a malformed table cannot make the kernel read outside the pages (the result
+ *   is then unspecified).
+ *   page_size: a power of two in [32, 1024] (a 32-key tile then never straddles a page).
+ *   workspace: at least attn_decode_workspace_size(B, H, max_pages * page_size, d) bytes.
+ * dtype must be ATTN_BF16; H / H_kv in {1, 2, 4, 8}; B * H_kv < 2^24.
+ */
+attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                              const int32_t* kv_len, const int32_t* block_table, int B, int H, int H_kv,
+                              int num_pages, int page_size, int max_pages, int d, float scale, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass: gradients of L = sum(O * dO) with respect to Q, K and V, recomputing the scores
  * from Q and K instead of reading a stored N x N matrix ("Why Fast GPUs Still Wait for Memory",
  * section "FlashAttention is an IO algorithm": the backward recomputes S). Every gradient element

@@ -34,6 +34,7 @@ SIGNATURES = {
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
+    "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_timing_enable": (_I, [_I]),
@@ -183,6 +184,38 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len
     _check(_lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(kv_len), B, H, H_kv,
                             N_cap, d, 0, float(scale), ATTN_BF16, _ptr(workspace), workspace.numel(),
                             _stream(q.device)))
+    return out, lse
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                 kv_len: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 want_lse: bool = True):
+    """Paged decode: q [B,H,d] bf16, pages [P,H_kv,page_size,d] bf16, block_table [B,max_pages] and
+    kv_len [B] int32 on the GPU. Returns (o, lse)."""
+    _need(q, "q", torch.bfloat16)
+    B, H, d = q.shape
+    P, H_kv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _need(k_pages, "k_pages", torch.bfloat16, (P, H_kv, page_size, d), q.device)
+    _need(v_pages, "v_pages", torch.bfloat16, (P, H_kv, page_size, d), q.device)
+    _need(block_table, "block_table", torch.int32, None, q.device)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    max_pages = block_table.shape[1]
+    _need(kv_len, "kv_len", torch.int32, (B,), q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = decode_workspace_size(B, H, max_pages * page_size, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(_lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse), _ptr(kv_len),
+                                  _ptr(block_table), B, H, H_kv, P, page_size, max_pages, d, float(scale), ATTN_BF16,
+                                  _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out, lse
 
 

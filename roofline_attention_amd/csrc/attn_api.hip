@@ -130,7 +130,7 @@ TimedScope::~TimedScope() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -236,6 +236,48 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
   return hip_status(ra::launch_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, workspace,
                                       static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                              const int32_t* kv_len, const int32_t* block_table, int B, int H, int H_kv,
+                              int num_pages, int page_size, int max_pages, int d, float scale, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !o || !kv_len || !block_table)
+    return fail(ATTN_ERR_INVALID_ARG, "q, k_pages, v_pages, o, kv_len and block_table must be non-null");
+  if (page_size < 32 || page_size > 1024 || (page_size & (page_size - 1)))
+    return fail(ATTN_ERR_UNSUPPORTED, "page_size must be a power of two in [32, 1024]");
+  if (num_pages < 1 || max_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1");
+  const long long n_cap = (long long)max_pages * page_size;
+  if (n_cap > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "max_pages * page_size exceeds 2^31 - 1");
+  const int N_cap = (int)n_cap;
+  attn_status st = check_shape(B, H, H_kv, N_cap, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports ATTN_BF16 only");
+  const int G = H / H_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ATTN_ERR_UNSUPPORTED, "decode group size H/H_kv must be 1, 2, 4 or 8");
+  if ((long long)B * H_kv >= (1LL << 24))
+    return fail(ATTN_ERR_INVALID_ARG, "decode needs B * H_kv < 2^24 (one grid row of workgroups)");
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, pages and o must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(kv_len) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "kv_len, block_table and lse must be 4-byte aligned");
+  const size_t need = ra::decode_workspace_bytes(B, H, N_cap, d);
+  if (workspace == nullptr || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "decode workspace too small");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t qb = (size_t)B * H * d * 2, pb = (size_t)num_pages * H_kv * page_size * d * 2;
+  const Range rq{q, qb}, rk{k_pages, pb}, rv{v_pages, pb}, ro{o, qb}, rl{lse, lse ? (size_t)B * H * 4 : 0},
+      rw{workspace, need}, rn{kv_len, (size_t)B * 4}, rt{block_table, (size_t)B * max_pages * 4};
+  const Range outs[] = {ro, rl, rw};
+  const Range ins[] = {rq, rk, rv, rn, rt};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
+  if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw))
+    return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
+  return hip_status(ra::launch_decode_paged(q, k_pages, v_pages, o, lse, kv_len, block_table, B, H, H_kv, num_pages,
+                                            page_size, max_pages, d, scale, workspace,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int N, int d) {

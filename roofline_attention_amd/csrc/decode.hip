@@ -45,6 +45,19 @@ __device__ __forceinline__ bf16x8 buffer_load16_nt(__amdgpu_buffer_rsrc_t rsrc, 
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voffset, 0, 2));
 }
 
+// Buffer resource over [base, base + bytes) whose inputs are wave-uniform by construction; the
+// readfirstlanes tell the compiler so, which keeps the descriptor in scalar registers (otherwise
+// a descriptor built from loaded values is treated as divergent and every load is wrapped in a
+// loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  // readfirstlane returns int: each half goes through uint32_t before widening, or the low half
+  // would be sign-extended into the high one.
+  const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return make_rsrc((const void*)(uintptr_t)ua, __builtin_amdgcn_readfirstlane(bytes));
+}
+
 template <int HD, int G>
 struct DecodeMerge {
   float m[DEC_WAVES][G];
@@ -64,11 +77,17 @@ struct DecodeMerge {
 //   V written to the wave's LDS tile and read back transposed as the A operand of
 //   O^T += V^T P^T (16x16x32 MFMAs).
 // Register loads of tiles past the wave's last key return zeros (buffer range check).
-template <int HD, int G>
+// PAGED: the caches are pages [num_pages, H_kv, 2^page_shift, d] and row j of sequence b lives in
+// page block_table[b * max_pages + j >> page_shift]; a 32-key tile never straddles a page (pages
+// hold a multiple of 32 rows), so each tile is one contiguous run read through its own buffer
+// resource. Page ids are looked up two tiles ahead of their loads and clamped into
+// [0, num_pages), so a malformed table cannot send a load outside the caches.
+template <int HD, int G, bool PAGED>
 __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
     const bf16* __restrict__ Qd, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int32_t* __restrict__ kv_len, float* __restrict__ ws, int H, int H_kv, int N_cap,
-    int n_split, float scale_log2) {
+    int n_split, float scale_log2, const int32_t* __restrict__ block_table, int max_pages, int page_shift,
+    int num_pages) {
   constexpr int CH = HD / 8;        // 16-byte chunks per row
   constexpr int KSTEPS = HD / 32;   // 16x16x32 k-steps over d
   constexpr int CB = HD / 16;       // 16-row blocks of O^T
@@ -108,9 +127,9 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
                      : bf16x8{};
   }
 
-  const size_t head = ((size_t)b * H_kv + hk) * (size_t)N_cap * HD;
-  const auto krs = make_rsrc(Kc + head + (size_t)kw_begin * HD, n_keys * HD * 2);
-  const auto vrs = make_rsrc(Vc + head + (size_t)kw_begin * HD, n_keys * HD * 2);
+  const size_t head = PAGED ? 0 : ((size_t)b * H_kv + hk) * (size_t)N_cap * HD;
+  const auto krs = make_rsrc(Kc + head + (size_t)kw_begin * HD, PAGED ? 0 : n_keys * HD * 2);
+  const auto vrs = make_rsrc(Vc + head + (size_t)kw_begin * HD, PAGED ? 0 : n_keys * HD * 2);
   // K A-operand of half h, k-step kk: row 16h + col, bytes (32kk + 8q4) * 2 of the row.
   const int k_off = col * HD * 2 + q4 * 16;
   // V rows: lane holds chunk (lane % CH) of row (lane / CH) + VROWS * i.
@@ -120,14 +139,35 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
     bf16x8 k[2][KSTEPS];
     bf16x8 v[VLOADS];
   };
-  auto load = [&](int t, Tile& tl) {
-    const int base = t * DEC_TILE * HD * 2;
+  // Physical page of tile t (PAGED only): the table entry is clamped to the table row, the id
+  // into [0, num_pages).
+  auto lookup = [&](int t) {
+    if constexpr (PAGED) {
+      const int j = min((kw_begin + t * DEC_TILE) >> page_shift, max_pages - 1);
+      // Same address in every lane: readfirstlane keeps the id (and the tile's buffer resource
+      // built from it) in scalar registers.
+      return __builtin_amdgcn_readfirstlane(min(max(block_table[(size_t)b * max_pages + j], 0), num_pages - 1));
+    } else {
+      return 0;
+    }
+  };
+  auto load = [&](int t, Tile& tl, int pid) {
+    int base = t * DEC_TILE * HD * 2;
+    auto kr = krs, vr = vrs;
+    if constexpr (PAGED) {
+      const int off = (kw_begin + t * DEC_TILE) & ((1 << page_shift) - 1);
+      const size_t row = (((size_t)pid * H_kv + hk) << page_shift) + off;
+      const int bytes = min(max(n_keys - t * DEC_TILE, 0), DEC_TILE) * HD * 2;  // 0 past the wave's keys
+      kr = uniform_rsrc(Kc + row * HD, bytes);
+      vr = uniform_rsrc(Vc + row * HD, bytes);
+      base = 0;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) tl.k[h][kk] = buffer_load16_nt(krs, base + k_off + h * 16 * HD * 2 + kk * 64);
+      for (int kk = 0; kk < KSTEPS; ++kk) tl.k[h][kk] = buffer_load16_nt(kr, base + k_off + h * 16 * HD * 2 + kk * 64);
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) tl.v[i] = buffer_load16_nt(vrs, base + v_off + i * VROWS * HD * 2);
+    for (int i = 0; i < VLOADS; ++i) tl.v[i] = buffer_load16_nt(vr, base + v_off + i * VROWS * HD * 2);
   };
 
   // V^T A-operand (transposed read): in 16-lane group q4, source lane 4e + j points at key row
@@ -209,13 +249,16 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
   // leaves m, l and O unchanged), so the wait before each consume covers only the tile it needs.
   {
     Tile ta, tb;
-    load(0, ta);
-    load(1, tb);
+    load(0, ta, lookup(0));
+    load(1, tb, lookup(1));
+    int pa = lookup(2), pb = lookup(3);  // page ids two tiles ahead of their loads
     for (int t = 0; t < n_tiles; t += 2) {
       consume(t, ta);
-      load(t + 2, ta);
+      load(t + 2, ta, pa);
+      pa = lookup(t + 4);
       consume(t + 1, tb);
-      load(t + 3, tb);
+      load(t + 3, tb, pb);
+      pb = lookup(t + 5);
     }
   }
 
@@ -334,16 +377,18 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   if (lse != nullptr && lane == 0) lse[(size_t)b * H + h] = (M + log2f(L)) * kLn2;
 }
 
-template <int HD, int G>
+template <int HD, int G, bool PAGED>
 hipError_t launch(const void* q, const void* kc, const void* vc, void* o, float* lse, const int32_t* kv_len,
                   int B, int H, int H_kv, int N_cap, float scale, void* ws, hipStream_t stream,
-                  const char* split_name, const char* combine_name) {
+                  const char* split_name, const char* combine_name, const int32_t* block_table, int max_pages,
+                  int page_shift, int num_pages) {
   const int n_split = (N_cap + kDecodeSplit - 1) / kDecodeSplit;
   {
     TimedScope ts(split_name, stream);
-    hipLaunchKernelGGL((decode_split_kernel<HD, G>), dim3(B * H_kv, n_split), dim3(DEC_WAVES * 64), 0, stream,
+    hipLaunchKernelGGL((decode_split_kernel<HD, G, PAGED>), dim3(B * H_kv, n_split), dim3(DEC_WAVES * 64), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(kc), static_cast<const bf16*>(vc),
-                       kv_len, static_cast<float*>(ws), H, H_kv, N_cap, n_split, scale * kLog2e);
+                       kv_len, static_cast<float*>(ws), H, H_kv, N_cap, n_split, scale * kLog2e, block_table,
+                       max_pages, page_shift, num_pages);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -355,19 +400,30 @@ hipError_t launch(const void* q, const void* kc, const void* vc, void* o, float*
   return hipGetLastError();
 }
 
-template <int HD>
+// Paging descriptor of one call (block_table == nullptr: contiguous caches).
+struct Pages {
+  const int32_t* table;
+  int max_pages, page_shift, num_pages;
+};
+
+template <int HD, bool PAGED>
 hipError_t launch_g(int G, const void* q, const void* kc, const void* vc, void* o, float* lse,
                     const int32_t* kv_len, int B, int H, int H_kv, int N_cap, float scale, void* ws,
-                    hipStream_t stream) {
+                    hipStream_t stream, const Pages& pg) {
+  const char* comb = "decode_combine";
   switch (G) {
-    case 1: return launch<HD, 1>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
-                                 "decode_split_g1", "decode_combine");
-    case 2: return launch<HD, 2>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
-                                 "decode_split_g2", "decode_combine");
-    case 4: return launch<HD, 4>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
-                                 "decode_split_g4", "decode_combine");
-    case 8: return launch<HD, 8>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
-                                 "decode_split_g8", "decode_combine");
+    case 1: return launch<HD, 1, PAGED>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
+                                        PAGED ? "decode_paged_split_g1" : "decode_split_g1", comb, pg.table,
+                                        pg.max_pages, pg.page_shift, pg.num_pages);
+    case 2: return launch<HD, 2, PAGED>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
+                                        PAGED ? "decode_paged_split_g2" : "decode_split_g2", comb, pg.table,
+                                        pg.max_pages, pg.page_shift, pg.num_pages);
+    case 4: return launch<HD, 4, PAGED>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
+                                        PAGED ? "decode_paged_split_g4" : "decode_split_g4", comb, pg.table,
+                                        pg.max_pages, pg.page_shift, pg.num_pages);
+    case 8: return launch<HD, 8, PAGED>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
+                                        PAGED ? "decode_paged_split_g8" : "decode_split_g8", comb, pg.table,
+                                        pg.max_pages, pg.page_shift, pg.num_pages);
     default: return hipErrorInvalidValue;
   }
 }
@@ -383,8 +439,23 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, float scale,
                          void* ws, hipStream_t stream) {
   const int G = H / H_kv;
-  return d == 128 ? launch_g<128>(G, q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream)
-                  : launch_g<64>(G, q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream);
+  const Pages none{nullptr, 1, 0, 1};
+  return d == 128 ? launch_g<128, false>(G, q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream, none)
+                  : launch_g<64, false>(G, q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream, none);
+}
+
+hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                               const int32_t* kv_len, const int32_t* block_table, int B, int H, int H_kv,
+                               int num_pages, int page_size, int max_pages, int d, float scale, void* ws,
+                               hipStream_t stream) {
+  const int G = H / H_kv;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const Pages pg{block_table, max_pages, shift, num_pages};
+  const int N_cap = max_pages * page_size;
+  return d == 128
+             ? launch_g<128, true>(G, q, k_pages, v_pages, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream, pg)
+             : launch_g<64, true>(G, q, k_pages, v_pages, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream, pg);
 }
 
 }  // namespace ra

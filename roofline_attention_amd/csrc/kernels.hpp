@@ -45,6 +45,14 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d,
                          float scale, void* ws, hipStream_t stream);
 
+// Paged caches: k_pages, v_pages [num_pages, H_kv, page_size, d], block_table [B, max_pages] of
+// physical page ids; page_size a power of two in [32, 1024]. Same workspace as launch_decode with
+// N_cap = max_pages * page_size.
+hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                               const int32_t* kv_len, const int32_t* block_table, int B, int H, int H_kv,
+                               int num_pages, int page_size, int max_pages, int d, float scale, void* ws,
+                               hipStream_t stream);
+
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, float* dq, float* dk, float* dv,

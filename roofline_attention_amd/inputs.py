@@ -160,6 +160,38 @@ def make_decode(w: Workload, nan_pad: bool = True) -> dict:
     return {"q": q, "k": k, "v": v, "kv_len": torch.from_numpy(kv_len)}
 
 
+def make_decode_paged(w: Workload, page_size: int, dense: Optional[dict] = None, spare_pages: int = 3) -> dict:
+    """The decode workload's caches cut into pages [P, H_kv, page_size, d] at shuffled physical slots.
+
+    Sequence b uses ceil(kv_len[b] / page_size) pages; the physical order is a seeded permutation,
+    `spare_pages` unreferenced NaN pages sit among them, rows past kv_len in a last page are NaN, and
+    unused block-table entries are -1. Returns q, k_pages, v_pages, block_table [B, max_pages],
+    kv_len (the same q and rows as make_decode).
+    """
+    if dense is None:
+        dense = make_decode(w)
+    kv_len = dense["kv_len"].numpy()
+    max_pages = (w.N + page_size - 1) // page_size
+    n_pages = [(int(n) + page_size - 1) // page_size for n in kv_len]
+    P = sum(n_pages) + spare_pages
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, TENSOR_KVLEN, page_size])))
+    slots = g.permutation(P)
+    dt = dense["k"].dtype
+    kp = torch.full((P, w.H_kv, page_size, w.d), float("nan"), dtype=dt)
+    vp = torch.full((P, w.H_kv, page_size, w.d), float("nan"), dtype=dt)
+    table = torch.full((w.B, max_pages), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(w.B):
+        for j in range(n_pages[b]):
+            phys = int(slots[nxt])
+            nxt += 1
+            r0, r1 = j * page_size, min((j + 1) * page_size, w.N)
+            kp[phys, :, :r1 - r0] = dense["k"][b, :, r0:r1]
+            vp[phys, :, :r1 - r0] = dense["v"][b, :, r0:r1]
+            table[b, j] = phys
+    return {"q": dense["q"], "k_pages": kp, "v_pages": vp, "block_table": table, "kv_len": dense["kv_len"]}
+
+
 def decode_head_slices(w: Workload, b: int, hk: int, length: int):
     """Regenerate the first `length` rows of one KV head of a decode cache (no NaN pad)."""
     rows = w.N

@@ -41,7 +41,7 @@ def test_binding_signatures_cover_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
     assert lib.attn_status_string(OK) == b"ATTN_OK"
     assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
     assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
@@ -123,6 +123,26 @@ def test_decode_validation(lib):
     assert call(d=80) == UNSUPPORTED
     assert call(B=65535, H=512, H_kv=512) == INVALID  # B * H_kv beyond one grid row
     assert lib.attn_decode_workspace_size(1, 1, 1, 96) == 0
+
+
+def test_decode_paged_validation(lib):
+    p = [addr(i) for i in range(8)]
+    ws_need = lib.attn_decode_workspace_size(64, 32, 128 * 64, 128)
+
+    def call(H=32, H_kv=8, P=1000, ps=64, max_pages=128, d=128, dtype=BF16, table=p[6], ws_bytes=ws_need):
+        return lib.attn_decode_paged(p[0], p[1], p[2], p[3], p[4], p[5], table, 64, H, H_kv, P, ps, max_pages, d,
+                                     0.088, dtype, p[7], ws_bytes, None)
+
+    assert call(table=None) == INVALID
+    assert call(ps=16) == UNSUPPORTED
+    assert call(ps=96) == UNSUPPORTED
+    assert call(ps=2048) == UNSUPPORTED
+    assert call(P=0) == INVALID
+    assert call(max_pages=0) == INVALID
+    assert call(ws_bytes=ws_need - 4) == WORKSPACE
+    assert call(H=48, H_kv=4) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(table=ctypes.c_void_p(BASE + 6 * GAP + 2)) == INVALID
 
 
 def test_bwd_validation(lib):

@@ -250,6 +250,40 @@ def test_decode_more_than_64_splits(lib):
     assert eo <= TOL_BF16 and el <= TOL_BF16
 
 
+@pytest.mark.parametrize("page_size", [32, 64, 256])
+@pytest.mark.parametrize("H,H_kv,d", [(8, 8, 128), (8, 4, 64), (16, 2, 128)])
+def test_decode_paged_matches_dense_and_oracle(lib, H, H_kv, d, page_size):
+    # Same rows as the contiguous cache, scattered over shuffled pages: the result must equal the
+    # contiguous decode bit for bit (same arithmetic, other addresses) and the paged oracle.
+    w = I.Workload("decp", "decode", 7, H, H_kv, 1100, d, "bf16", False, seed=16, kv_lo=1, kv_hi=1100)
+    dense = I.make_decode(w, nan_pad=False)
+    dense["kv_len"] = torch.tensor([1, 255, 257, 1023, 1024, 1025, 1100], dtype=torch.int32)
+    for b in range(w.B):
+        n = int(dense["kv_len"][b])
+        dense["k"][b, :, n:] = float("nan")
+        dense["v"][b, :, n:] = float("nan")
+    t = I.make_decode_paged(w, page_size, dense=dense)
+    o, lse = lib.decode_paged(dev(t["q"]), dev(t["k_pages"]), dev(t["v_pages"]), dev(t["block_table"]),
+                              dev(t["kv_len"]), w.scale)
+    od, lsed = lib.decode(dev(dense["q"]), dev(dense["k"]), dev(dense["v"]), dev(dense["kv_len"]), w.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    assert torch.equal(o.cpu(), od.cpu()) and torch.equal(lse.cpu(), lsed.cpu())
+    ro, rl = orc.attention_decode_paged(f64(t["q"]), t["k_pages"].float().numpy(), t["v_pages"].float().numpy(),
+                                        t["block_table"].numpy(), t["kv_len"].numpy(), w.scale)
+    assert max_err(o.cpu(), ro) <= TOL_BF16 and max_err(lse.cpu(), rl) <= TOL_BF16
+
+
+def test_decode_paged_full_workload_matches_dense(lib):
+    w = I.WORKLOADS["decode_gqa"]
+    dense = I.make_decode(w)
+    t = I.make_decode_paged(w, 64, dense=dense)
+    o, lse = lib.decode_paged(dev(t["q"]), dev(t["k_pages"]), dev(t["v_pages"]), dev(t["block_table"]),
+                              dev(t["kv_len"]), w.scale)
+    od, lsed = lib.decode(dev(dense["q"]), dev(dense["k"]), dev(dense["v"]), dev(dense["kv_len"]), w.scale)
+    assert torch.equal(o.cpu(), od.cpu()) and torch.equal(lse.cpu(), lsed.cpu())
+    assert torch.isfinite(o.float()).all()
+
+
 def test_decode_zero_length_is_defined(lib):
     w = I.Workload("dec0", "decode", 2, 4, 4, 64, 128, "bf16", False, seed=17, kv_lo=1, kv_hi=64)
     t = I.make_decode(w)
