@@ -51,7 +51,14 @@ struct FwdSmem {
 };
 
 template <int HD>
-__device__ __forceinline__ int swz_k(int r) { return r & (HD / 8 - 1); }
+__device__ __forceinline__ int swz_k(int r) {
+  // A 16-lane b128 read touches rows r..r+15 at one chunk. 256-byte rows (d = 128) all start in
+  // bank 0, so 16 distinct chunk positions suffice; 128-byte rows (d = 64) alternate between the
+  // two bank halves by row parity, so rows r and r+8 need distinct positions: key the swizzle on
+  // r / 2 (period 16 rows either way).
+  if constexpr (HD == 128) return r & 15;
+  else return (r >> 1) & 7;
+}
 template <int HD>
 __device__ __forceinline__ int swz_v(int r) {
   if constexpr (HD == 128) return 4 * (r & 3) + 2 * ((r >> 1) & 1);
