@@ -27,6 +27,8 @@
 // nothing to any stored gradient, so only the causal diagonal needs a mask.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_tile.hpp"
@@ -405,41 +407,51 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
 
     const int q_end = min(N, qt * 128 + 128);
     const int n_kt = CAUSAL ? (q_end + BWD_BK - 1) / BWD_BK : (N + BWD_BK - 1) / BWD_BK;
-    stage(0, 0);
-    for (int t = 0; t < n_kt; ++t) {
+    // One key tile from LDS stage s; MASK applies the causal mask, needed only on the last two key
+    // tiles: every key of a tile below them precedes the workgroup's first query (n_kt - 2 <= 2 qt).
+    auto tile = [&](int s, int t, auto MASK_) {
+      constexpr bool MASK = decltype(MASK_)::value;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (t + 1 < n_kt) stage(t + 1, (t + 1) & 1);
-      const int s = t & 1;
+      if (t + 1 < n_kt) stage(t + 1, 1 - s);
       const int k0 = t * BWD_BK;
-      const bool diag = CAUSAL && k0 + BWD_BK - 1 > q0;
-      bf16x8 dsb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // S^T and dP^T: lane column = query, rows = keys k0 + 32kb + 8(r/4) + 4g + r%4.
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        // S^T and dP^T: lane column = query, rows = keys k0 + 32kb + 8(r/4) + 4g + r%4. The first
+        // k-step takes a zero accumulator operand directly (no zero-filled registers).
         const bf16* krow = sm.k[s] + kb * 32 * HD + row_off;
         const bf16* vrow = sm.v[s] + kb * 32 * HD + row_off;
+        f32x16 sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + (0 ^ krow_t) * 8), qf[0], f32x16{});
+        f32x16 dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + (0 ^ vrow_t) * 8), df[0], f32x16{});
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
+        for (int kk = 1; kk < KSTEPS; ++kk) {
           sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ krow_t) * 8), qf[kk], sacc);
           dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + ((2 * kk) ^ vrow_t) * 8), df[kk], dpacc);
         }
+        bf16x8 dsb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(sacc[r], scale_log2, -lse2));
-          if (diag && k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p = 0.f;
-          dsb[2 * kb + (r >> 3)][r & 7] = to_bf16(p * (dpacc[r] - Dq));
+          if (MASK && k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p = 0.f;
+          dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - Dq));
+        }
+        // dQ^T += K^T dS^T for this block's 32 keys: A = K^T (rows c = 32cb + l32 by transposed
+        // read of the key tile), k-steps 2kb, 2kb + 1.
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb)
+            acc[cb] = mfma32(tr_operand<HD>(sm.k[s], tl, 32 * kb + 16 * hh, cb), dsb[hh], acc[cb]);
         }
       }
-      // dQ^T += K^T dS^T: A = K^T (rows c = 32cb + l32 by transposed read of the key tile).
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb)
-          acc[cb] = mfma32(tr_operand<HD>(sm.k[s], tl, 16 * ks, cb), dsb[ks], acc[cb]);
-      }
-    }
+    };
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    const int t_mask = CAUSAL ? max(0, n_kt - 2) : n_kt;
+    stage(0, 0);
+    int t = 0;
+    for (; t < t_mask; ++t) tile(t & 1, t, NoMask{});
+    for (; t < n_kt; ++t) tile(t & 1, t, Mask{});
 
     if (qi < N) {
       float* out = dQ + head + (size_t)qi * HD;
