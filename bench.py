@@ -180,7 +180,8 @@ def main():
         "fwd_bf16_d128_causal": ("mfma", 4.0 * Nsq),
         "bwd_dkdv_d128_causal": ("mfma", 8.0 * Nsq),
         "bwd_dq_d128_causal": ("mfma", 2.0 * Nsq),
-        "bwd_pre_d128": ("hbm", 2.0 * 2 * w.B * w.H * w.N * w.d + 4.0 * w.B * w.H * w.N),
+        # reads O, dO and LSE; writes D and LSE * log2 e
+        "bwd_pre_d128": ("hbm", 2.0 * 2 * w.B * w.H * w.N * w.d + 12.0 * w.B * w.H * w.N),
     }
     kernels = {}
     for name, st in stats.items():

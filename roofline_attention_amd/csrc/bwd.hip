@@ -10,7 +10,7 @@
 // doubled DRAM traffic in the same paper (section 4.7).
 //
 // Kernels, per (batch, head):
-//   bwd_pre : D_i = sum_t dO[i,t] * O[i,t]   (equals sum_j P_ij dP_ij)
+//   bwd_pre : D_i = sum_t dO[i,t] * O[i,t]   (equals sum_j P_ij dP_ij), and LSE_i * log2 e
 //   bwd_dkdv: workgroup = 128 keys (4 waves x 32, K and V of its keys in registers); streams
 //             64-query tiles of Q, dO, LSE and D through three LDS stages:
 //             S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e), dV += P^T dO, dP = dO V^T,
@@ -57,7 +57,9 @@ constexpr int BWD_BK = 64;   // keys per staged tile in the query-major kernel
 template <int HD>
 __global__ __launch_bounds__(BWD_THREADS) void bwd_pre_kernel(const bf16* __restrict__ O,
                                                               const bf16* __restrict__ dO,
-                                                              float* __restrict__ D, long long rows) {
+                                                              const float* __restrict__ LSE,
+                                                              float* __restrict__ D, float* __restrict__ L2,
+                                                              long long rows) {
   constexpr int CH = HD / 8;
   constexpr int RPB = BWD_THREADS / CH;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CH;
@@ -74,7 +76,10 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_pre_kernel(const bf16* __rest
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));
   if constexpr (CH == 16)
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true));
-  if (row < rows && c == 0) D[row] = x;
+  if (row < rows && c == 0) {
+    D[row] = x;
+    L2[row] = LSE[row] * kLog2e;  // the row's LSE in log2 units, streamed by the key-major kernel
+  }
 }
 
 // Per-lane constants of the transposed read over a [rows][HD] tile with swizzle SWZ: in its
@@ -134,7 +139,7 @@ struct DkdvSmem {
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, int H, int group, int N, int n_ktiles, float scale,
     float scale_log2) {
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e] * kLog2e));
+          float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e]));  // l4: LSE * log2 e
           if (mask && key > 32 * u + 8 * rg + 4 * g + e) p = 0.f;
           pb[r >> 3][r & 7] = to_bf16(p);
           dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - d4[e]));
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
       const size_t qrows = (size_t)b * H + (size_t)hk * group + j;
       Qh = Q + qrows * N * HD;
       dOh = dO + qrows * N * HD;
-      LSEh = LSE + qrows * N;
+      LSEh = LSE2 + qrows * N;  // LSE * log2 e, from the preprocess
       Dh = Dg + qrows * N;
       // Every wave has finished reading the previous head's tiles before this head's prologue
       // writes LDS.
@@ -478,13 +483,14 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   const bf16* V = static_cast<const bf16*>(v);
   const bf16* O = static_cast<const bf16*>(o);
   const bf16* dO = static_cast<const bf16*>(dout);
-  float* D = static_cast<float*>(ws);
   const long long rows = (long long)B * H * N;
+  float* D = static_cast<float*>(ws);  // workspace: D [B,H,N], then LSE * log2 e [B,H,N]
+  float* L2 = D + rows;
   constexpr int RPB = BWD_THREADS / (HD / 8);
   {
     TimedScope ts(pre_name, stream);
     hipLaunchKernelGGL((bwd_pre_kernel<HD>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(BWD_THREADS), 0,
-                       stream, O, dO, D, rows);
+                       stream, O, dO, lse, D, L2, rows);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -504,7 +510,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   {
     TimedScope ts(dkdv_name, stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total_kv), dim3(BWD_THREADS), dkdv_smem, stream, Q, K,
-                       V, dO, lse, D, dk, dv, H, H / H_kv, N, n_t, scale, scale * kLog2e);
+                       V, dO, L2, D, dk, dv, H, H / H_kv, N, n_t, scale, scale * kLog2e);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -520,7 +526,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
-  return (size_t)B * H * N * sizeof(float);
+  return 2 * (size_t)B * H * N * sizeof(float);  // D and LSE * log2 e per query row
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -148,7 +148,7 @@ def test_decode_paged_validation(lib):
 def test_bwd_validation(lib):
     p = [addr(i) for i in range(11)]
     need = lib.attn_bwd_workspace_size(2, 16, 4096, 128)
-    assert need == 2 * 16 * 4096 * 4
+    assert need == 2 * 2 * 16 * 4096 * 4  # D and LSE*log2(e) per query row
 
     def call(H=16, H_kv=16, dtype=BF16, ws_bytes=need, lse=p[5]):
         return lib.attn_bwd(p[0], p[1], p[2], p[3], p[4], lse, p[6], p[7], p[8], 2, H, H_kv, 4096, 128, 1, 0.088,
