@@ -26,6 +26,13 @@ design notes):
   * a ragged (variable-length) batch packs its sequences' rows one after another
     ([T, H, d], offsets cu_seqlens); each sequence attends only within itself, and a
     causal position is counted from the sequence's first row;
+  * fp8 inputs are OCP FP8 E4M3 codes (the "FN" variant: exponent bias 7, no
+    infinities, S.1111.111 is NaN, largest finite value 448), the e4m3 format of
+    "FP8 Formats for Deep Learning" (in the same page's sources), with one
+    float32 descale factor per tensor (real value = descale * decoded code); the
+    result is exact attention of those real values ("Why Fast GPUs Still Wait for
+    Memory" names fp8 only through its doubled compute ceiling, section "pi is the
+    top of a stack" and Table 1, and leaves the format and its scaling metadata open);
   * the backward pass is the gradient of L = sum(O * dO) with respect to Q, K
     and V, recomputing P from an explicit S (same page: "the backward pass does
     more arithmetic, because S is recomputed rather than stored"; the MoA paper,
@@ -115,8 +122,8 @@ def attention_fwd_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
     q [T, H, d], k/v [T, H_kv, d]; sequence b owns rows cu_seqlens[b] .. cu_seqlens[b+1] - 1
     and attends only within itself, with positions counted from its own first row (causal:
     key j <= query i within the sequence). Returns o [T, H, d] and lse [H, T]. The definition of
-    "Attention from first principles" is applied to each sequence on its own, the way SURVEY's
-    next step f1 (ragged batches by per-sequence offsets) reads the grouped prefill.
+    "Attention from first principles" is applied to each sequence on its own: a ragged batch is
+    a set of independent sequences addressed by per-sequence offsets.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     T, H, d = q.shape
@@ -163,6 +170,44 @@ def attention_fwd_varlen_rows(q, k, v, cu_seqlens, causal: bool, scale: float, r
         o[r] = p[0] @ v[r0:k_end, hk]
         lse[r] = lse_r[0]
     return o, lse
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Real values (float64) of OCP FP8 E4M3 codes given as uint8.
+
+    Bit layout S.EEEE.MMM, exponent bias 7: E = 0 is subnormal, (-1)^S * (M / 8) * 2^-6;
+    otherwise (-1)^S * (1 + M / 8) * 2^(E - 7), except E = 15 with M = 7, which is NaN
+    (the FN variant has no infinities, so its largest finite value is 1.75 * 2^8 = 448).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >= 128, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def _fp8_real(q8, k8, v8, descale):
+    dq, dk, dv = (float(x) for x in descale)
+    return dq * e4m3_decode(q8), dk * e4m3_decode(k8), dv * e4m3_decode(v8)
+
+
+def attention_fwd_fp8(q8, k8, v8, descale, causal: bool, scale: float):
+    """Exact attention of fp8 (E4M3) inputs: O [B,H,N,d] and LSE [B,H,N] in float64.
+
+    q8 [B,H,N,d], k8/v8 [B,H_kv,N,d] are uint8 E4M3 codes and descale = (dq, dk, dv) the
+    per-tensor factors, so the real inputs are dq * decode(q8), and so on. The attention of
+    those real values is the plain definition, computed by attention_fwd.
+    """
+    q, k, v = _fp8_real(q8, k8, v8, descale)
+    return attention_fwd(q, k, v, causal, scale)
+
+
+def attention_fwd_fp8_rows(q8, k8, v8, descale, causal: bool, scale: float, rows):
+    """attention_fwd_rows of the real values of fp8 inputs, for selected (b, h, i) rows."""
+    q, k, v = _fp8_real(q8, k8, v8, descale)
+    return attention_fwd_rows(q, k, v, causal, scale, rows)
 
 
 def attention_decode(q, k_cache, v_cache, kv_len, scale: float):

@@ -20,7 +20,12 @@ Recipe (the pages fix none of it; the workloads are synthetic sweeps shaped like
   or beyond a sequence's length are filled with NaN so that any read of them
   shows up in the result;
 * a ragged prefill batch draws its lengths from the same length stream and packs
-  the (b, h) blocks of each tensor row after row ([T, H, d], offsets cu_seqlens).
+  the (b, h) blocks of each tensor row after row ([T, H, d], offsets cu_seqlens);
+* fp8 (E4M3) storage: each tensor's float32 sample is divided by a per-tensor
+  power-of-two descale, the smallest with amax / descale <= 448 (so the division
+  is exact and nothing saturates), and rounded to nearest even by torch's
+  float32 -> float8_e4m3fn cast; the codes are kept as uint8 and the descale is
+  handed to both sides.
 """
 from __future__ import annotations
 
@@ -45,7 +50,7 @@ class Workload:
     H_kv: int
     N: int  # sequence length (prefill) or cache capacity (decode)
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "e4m3"
     causal: bool
     seed: int
     qk_factor: float = 1.0  # exact factor applied to Q and K samples
@@ -72,6 +77,10 @@ WORKLOADS = {
     "fwdbwd_4k_causal": Workload("fwdbwd_4k_causal", "fwdbwd", 2, 16, 16, 4096, 128, "bf16", True, seed=5),
     # Ragged prefill (packed rows, per-sequence offsets): 16 sequences with the decode length mix,
     # grouped heads 32/8; N is the longest length the grid must cover.
+    # The large prefill with fp8 (E4M3) inputs and per-tensor descales.
+    "prefill_4k_causal_fp8": Workload("prefill_4k_causal_fp8", "fwd", 2, 32, 32, 4096, 128, "e4m3", True, seed=7,
+                                      qk_factor=0.5),
+    "prefill_4k_fp8": Workload("prefill_4k_fp8", "fwd", 2, 32, 32, 4096, 128, "e4m3", False, seed=7, qk_factor=0.5),
     "prefill_varlen": Workload("prefill_varlen", "varlen", 16, 32, 8, 8192, 128, "bf16", True, seed=6,
                                kv_lo=512, kv_hi=8192),
 }
@@ -98,6 +107,26 @@ def make_tensor(seed: int, tensor_id: int, B: int, H: int, rows: int, d: int, dt
         for h in range(H):
             blk = torch.from_numpy(normal_block(seed, tensor_id, b, h, (rows, d), factor))
             out[b, h].copy_(blk)  # float32 -> bf16 cast rounds to nearest even
+    return out
+
+
+def fp8_codes(x: torch.Tensor):
+    """(uint8 E4M3 codes, descale) for a float32 tensor, with a power-of-two descale."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
+    codes = (x / descale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, descale
+
+
+def make_fp8_prefill(w: Workload) -> dict:
+    """q, k, v as uint8 E4M3 codes [B,H,N,d] / [B,H_kv,N,d] and descale = (dq, dk, dv)."""
+    out, ds = {}, []
+    for name, tid, heads, f in (("q", TENSOR_Q, w.H, w.qk_factor), ("k", TENSOR_K, w.H_kv, w.qk_factor),
+                                ("v", TENSOR_V, w.H_kv, 1.0)):
+        x = make_tensor(w.seed, tid, w.B, heads, w.N, w.d, "f32", f)
+        out[name], s = fp8_codes(x)
+        ds.append(s)
+    out["descale"] = tuple(ds)
     return out
 
 

@@ -37,6 +37,13 @@ MUTANTS = {
     "paged_wrong_page": ("pages = table[b, :(n + ps - 1) // ps]", "pages = table[b, 1:(n + ps - 1) // ps + 1]"),
     "paged_reads_first_head": ("np.asarray(k_pages[p, hk], dtype=np.float64) for p in pages",
                                "np.asarray(k_pages[p, 0], dtype=np.float64) for p in pages"),
+    "e4m3_bias_8": ("(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)"),
+    "e4m3_subnormal_implicit_one": ("(m / 8.0) * 2.0 ** -6", "(1.0 + m / 8.0) * 2.0 ** -6"),
+    "e4m3_sign_threshold_off_by_one": ("sign = np.where(c >= 128, -1.0, 1.0)", "sign = np.where(c >= 129, -1.0, 1.0)"),
+    "fp8_v_descale_dropped": ("dq * e4m3_decode(q8), dk * e4m3_decode(k8), dv * e4m3_decode(v8)",
+                              "dq * e4m3_decode(q8), dk * e4m3_decode(k8), e4m3_decode(v8)"),
+    "fp8_k_uses_q_descale": ("dq * e4m3_decode(q8), dk * e4m3_decode(k8), dv * e4m3_decode(v8)",
+                             "dq * e4m3_decode(q8), dq * e4m3_decode(k8), dv * e4m3_decode(v8)"),
     "decode_reads_one_short": ("kh = np.asarray(k_cache[b, hk, :n], dtype=np.float64)",
                                "kh = np.asarray(k_cache[b, hk, :n - 1], dtype=np.float64)"),
 }
@@ -64,6 +71,11 @@ PIN_CALLS = [
     (pins.test_varlen_rows_agree_with_full, dict(causal=True)),
     (pins.test_decode_paged_equals_contiguous, dict(shuffle=True)),
     (pins.test_decode_paged_matches_sdpa, {}),
+    (pins.test_e4m3_decode_matches_torch_on_every_code, {}),
+    (pins.test_e4m3_decode_closed_forms, {}),
+    (pins.test_fp8_fwd_matches_torch_decode_and_sdpa, dict(causal=True)),
+    (pins.test_fp8_descales_enter_as_exact_factors, {}),
+    (pins.test_fp8_rows_agree_with_full, {}),
 ]
 
 

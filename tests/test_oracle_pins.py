@@ -402,3 +402,86 @@ def test_varlen_rows_agree_with_full(causal):
     np.testing.assert_allclose(ro, o[rows[:, 0], rows[:, 1]], atol=1e-13)
     np.testing.assert_allclose(rl, lse[rows[:, 1], rows[:, 0]], atol=1e-13)
 
+
+
+# ---------------------------------------------------------------- fp8 (E4M3) ---
+# The format is OCP FP8 E4M3 (FN variant), the e4m3 of "FP8 Formats for Deep Learning" (listed
+# among the sources of "Why Fast GPUs Still Wait for Memory"): bias 7, no infinities, NaN at
+# S.1111.111, largest finite 448, subnormals (M / 8) * 2^-6.
+
+ALL_CODES = np.arange(256, dtype=np.uint8)
+
+
+def torch_e4m3(codes):
+    """Library decode: torch's float8_e4m3fn -> float64 upcast (shares nothing with the oracle)."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    a, b = orc.e4m3_decode(ALL_CODES), torch_e4m3(ALL_CODES)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+    assert np.array_equal(np.signbit(a[~np.isnan(a)]), np.signbit(b[~np.isnan(b)]))  # -0 too
+
+
+def test_e4m3_decode_closed_forms():
+    d = orc.e4m3_decode
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0        # largest finite: 1.75 * 2^8
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9  # subnormals: M * 2^-9
+    assert d(0x08) == 2.0 ** -6                         # smallest normal
+    assert d(0x38) == 1.0 and d(0x3F) == 1.875 and d(0x40) == 2.0 and d(0xB8) == -1.0
+    assert d(0x00) == 0.0 and np.signbit(d(0x80)) and d(0x80) == 0.0
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    assert d(0x78) == 256.0 and d(0x77) == 240.0        # E = 15 is a finite binade except M = 7
+    pos = orc.e4m3_decode(np.arange(127, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)                     # codes 0..126 increase strictly
+    assert np.array_equal(orc.e4m3_decode(ALL_CODES[128:255]), -pos)
+    # within a binade the 8 steps are equal: 2^(E - 7) / 8
+    for e in range(1, 16):
+        vals = orc.e4m3_decode(np.array([(e << 3) | m for m in range(7 if e == 15 else 8)], dtype=np.uint8))
+        assert np.allclose(np.diff(vals), 2.0 ** (e - 7) / 8, rtol=0, atol=0)
+
+
+def fp8_case(B, H, H_kv, N, d, seed=0):
+    g = np.random.default_rng(seed)
+    # finite codes only (0x7F / 0xFF are NaN)
+    draw = lambda *s: np.where((c := g.integers(0, 256, size=s, dtype=np.uint8)) & 0x7F == 0x7F, c ^ 1, c).astype(np.uint8)
+    return draw(B, H, N, d), draw(B, H_kv, N, d), draw(B, H_kv, N, d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_fwd_matches_torch_decode_and_sdpa(causal):
+    q8, k8, v8 = fp8_case(2, 4, 2, 19, 16)
+    # random codes span 2^-9 .. 448; a small scale keeps the softmax from saturating to one-hot
+    ds, scale = (0.01, 0.02, 0.5), 0.07
+    o, lse = orc.attention_fwd_fp8(q8, k8, v8, ds, causal, scale)
+    q, k, v = (f * torch_e4m3(x) for f, x in zip(ds, (q8, k8, v8)))
+    np.testing.assert_allclose(o, sdpa(q, k, v, causal, scale), rtol=1e-12, atol=1e-12)
+    s = scale * np.einsum("bhid,bhjd->bhij", q, np.repeat(k, 2, axis=1))
+    if causal:
+        s = np.where(np.tril(np.ones((19, 19), dtype=bool)), s, -np.inf)
+    mx = s.max(-1, keepdims=True)
+    np.testing.assert_allclose(lse, (mx + np.log(np.exp(s - mx).sum(-1, keepdims=True)))[..., 0], rtol=1e-12)
+
+
+def test_fp8_descales_enter_as_exact_factors():
+    q8, k8, v8 = fp8_case(1, 2, 2, 11, 8, seed=1)
+    o1, l1 = orc.attention_fwd_fp8(q8, k8, v8, (0.01, 0.02, 1.0), True, 0.1)
+    o2, l2 = orc.attention_fwd_fp8(q8, k8, v8, (0.01, 0.02, 4.0), True, 0.1)   # V descale scales O only
+    np.testing.assert_array_equal(o2, 4.0 * o1)
+    np.testing.assert_array_equal(l2, l1)
+    o3, l3 = orc.attention_fwd_fp8(q8, k8, v8, (0.02, 0.01, 1.0), True, 0.1)   # only dq * dk matters
+    np.testing.assert_allclose(o3, o1, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(l3, l1, rtol=1e-14)
+    o4, l4 = orc.attention_fwd_fp8(q8, k8, v8, (0.01, 0.04, 1.0), True, 0.05)  # ... times the scale
+    np.testing.assert_allclose(o4, o1, rtol=1e-14, atol=1e-14)
+
+
+def test_fp8_rows_agree_with_full():
+    q8, k8, v8 = fp8_case(2, 4, 1, 13, 8, seed=2)
+    ds = (0.03, 0.01, 0.25)
+    o, lse = orc.attention_fwd_fp8(q8, k8, v8, ds, True, 0.2)
+    rows = np.array([(0, 0, 0), (1, 3, 12), (0, 2, 5), (1, 1, 7)])
+    ro, rl = orc.attention_fwd_fp8_rows(q8, k8, v8, ds, True, 0.2, rows)
+    np.testing.assert_allclose(ro, o[rows[:, 0], rows[:, 1], rows[:, 2]], atol=1e-13)
+    np.testing.assert_allclose(rl, lse[rows[:, 0], rows[:, 1], rows[:, 2]], atol=1e-13)
