@@ -244,8 +244,8 @@ def main():
 
 
 def run_legs(torch, lib, I, L, reps=20):
-    """Extra legs: the 4k prefill forward (causal and not), the 1k causal prefill, the ragged
-    prefill, GQA decode over a contiguous and over a paged cache."""
+    """Extra legs: the 4k prefill forward (causal and not; bf16, then fp8 inputs), the 1k causal
+    prefill, the ragged prefill, GQA decode over a contiguous and over a paged cache."""
     legs = {}
     for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
         w = I.WORKLOADS[name]
@@ -263,6 +263,27 @@ def run_legs(torch, lib, I, L, reps=20):
                       "wall_ms_per_call": wall / reps * 1e3}
         log(f"[bench] leg {name}: {legs[name]['avg_ms']:.3f} ms, {legs[name]['tflops']:.1f} TFLOP/s")
         del t, o, lse
+        torch.cuda.empty_cache()
+
+    # fp8 (E4M3) inputs: the same 4k prefill, priced against the fp8 matrix-core peak
+    for name in ("prefill_4k_causal_fp8", "prefill_4k_fp8"):
+        w = I.WORKLOADS[name]
+        t8 = I.make_fp8_prefill(w)
+        ds = t8.pop("descale")
+        t = {k: x.cuda() for k, x in t8.items()}
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        fn = lambda: lib.fwd_fp8(t["q"], t["k"], t["v"], ds, w.causal, w.scale, out=o, lse=lse)  # noqa: E731
+        for _ in range(3):
+            fn()
+        wall, stats = time_region(torch, lib, fn, reps)
+        (kname, st), = stats.items()
+        fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
+        tf = fl / (st["avg_ms"] * 1e-3) / 1e12
+        legs[name] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": tf, "frac_of_peak": tf / L.PEAK_FP8_TFLOPS,
+                      "peak_tflops": L.PEAK_FP8_TFLOPS, "wall_ms_per_call": wall / reps * 1e3}
+        log(f"[bench] leg {name}: {st['avg_ms']:.3f} ms, {tf:.1f} TFLOP/s ({tf / L.PEAK_FP8_TFLOPS:.3f} of fp8 peak)")
+        del t, t8, o, lse
         torch.cuda.empty_cache()
 
     w = I.WORKLOADS["prefill_varlen"]

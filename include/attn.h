@@ -72,6 +72,25 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int dtype, void* stream);
 
 /*
+ * fp8 forward: the same attention for inputs stored as 8-bit floats, which double the matrix-core
+ * ceiling ("Why Fast GPUs Still Wait for Memory", section "pi is the top of a stack" and Table 1:
+ * fp8 doubles pi and the ridge point). The pages leave the format and its scaling metadata open;
+ * this entry point takes OCP FP8 E4M3 codes (exponent bias 7, no infinities, S.1111.111 = NaN,
+ * largest finite 448) with one float32 descale factor per tensor:
+ *   real Q = q_descale * decode(q), real K = k_descale * decode(k), real V = v_descale * decode(v),
+ *   O = softmax(scale * Q K^T [causal]) V of those real values, LSE as for attn_fwd.
+ *   q [B, H, N, d], k, v [B, H_kv, N, d]: uint8 codes; o [B, H, N, d] bfloat16 (nearest even);
+ *   lse [B, H, N] float32 or NULL. d must be 128. Descales must be finite (any sign or zero).
+ * Accuracy: scores are exact products of the codes accumulated in float32; the probabilities that
+ * multiply V are rounded to E4M3 (relative error at most 2^-4 each, values below 2^-12 of the row
+ * maximum with an absolute error of at most 2^-16 of it), while the normaliser and LSE use the
+ * unrounded float32 probabilities. NaN codes propagate to the rows they reach.
+ */
+attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int H_kv, int N, int d, int causal, float scale,
+                         float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
  * Ragged (variable-length) prefill: B sequences of different lengths packed row after row, with
  * no padding. A padded batch of ragged sequences runs partly empty ("Why Fast GPUs Still Wait for
  * Memory", section "Shapes matter", trap "B* is not a batch size you can actually run"); here each

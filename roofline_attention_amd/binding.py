@@ -31,6 +31,7 @@ SIGNATURES = {
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
@@ -119,6 +120,34 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, scale: 
         _need(lse, "lse", torch.float32, (B, H, N), q.device)
     _check(_lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, N, d, int(bool(causal)),
                          float(scale), _DTYPES[q.dtype], _stream(q.device)))
+    return out, lse
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, descale, causal: bool, scale: Optional[float] = None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """fp8 forward: q [B,H,N,d], k/v [B,H_kv,N,d] uint8 E4M3 codes, descale = (q, k, v) float factors.
+
+    Returns (o bf16 [B,H,N,d], lse float32 [B,H,N] or None).
+    """
+    _need(q, "q", torch.uint8)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    _need(k, "k", torch.uint8, (B, H_kv, N, d), q.device)
+    _need(v, "v", torch.uint8, (B, H_kv, N, d), q.device)
+    dq, dk, dv = (float(x) for x in descale)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, H, N, d), q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    _check(_lib.attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, N, d, int(bool(causal)),
+                             float(scale), dq, dk, dv, _stream(q.device)))
     return out, lse
 
 

@@ -1,6 +1,7 @@
 // C-ABI layer of libroofattn.so: argument validation, dispatch to the kernel launchers, status
 // strings and the opt-in kernel timer. Every check runs before any HIP call, so a rejected call
 // has no side effects on the device.
+#include <float.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -130,7 +131,7 @@ TimedScope::~TimedScope() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 3; }
+int attn_abi_version(void) { return 4; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -170,6 +171,30 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return hip_status(ra::launch_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0, scale, s));
 }
 
+attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+                         int N, int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
+                         void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  attn_status st = check_shape(B, H, H_kv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "the fp8 forward supports d = 128 only");
+  if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
+    return fail(ATTN_ERR_INVALID_ARG, "descale factors must be finite");
+  if (!(fabs((double)scale * q_descale * k_descale * 1.4426950408889634) <= (double)FLT_MAX))
+    return fail(ATTN_ERR_INVALID_ARG, "scale * q_descale * k_descale overflows float32");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t qb = (size_t)B * H * N * d, kb = (size_t)B * H_kv * N * d, ob = qb * 2, lb = (size_t)B * H * N * 4;
+  const Range rq{q, qb}, rk{k, kb}, rv{v, kb}, ro{o, ob}, rl{lse, lse ? lb : 0};
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) || overlap(rl, rk) ||
+      overlap(rl, rv) || overlap(rl, ro))
+    return fail(ATTN_ERR_INVALID_ARG, "outputs overlap inputs or each other");
+  const long long tiles = (long long)((N + 127) / 128) * H * B;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  return hip_status(ra::launch_fwd_fp8(q, k, v, o, lse, B, H, H_kv, N, causal != 0, scale, q_descale, k_descale,
+                                       v_descale, static_cast<hipStream_t>(stream)));
+}
 
 attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                             const int32_t* cu_seqlens, int B, int max_seqlen, int T, int H, int H_kv, int d,

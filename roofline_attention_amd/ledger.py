@@ -14,11 +14,13 @@ The backward counts the five N^2 d products a non-materialising backward needs (
 dV, dK, dQ): W_bwd = 2.5 W_fwd. Recompute beyond those is implementation cost, not work.
 
 MI355X peaks (AMD's published figures, not on the pages): dense bf16 MFMA 2516.6 TFLOP/s
-(256 CU x 2.4 GHz x 4096 FLOP/clk/CU), HBM3E 8.0 TB/s.
+(256 CU x 2.4 GHz x 4096 FLOP/clk/CU), dense fp8 MFMA 5033.2 TFLOP/s (twice bf16, as the pages
+say of fp8 in general: section "pi is the top of a stack", Table 1), HBM3E 8.0 TB/s.
 """
 from __future__ import annotations
 
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 

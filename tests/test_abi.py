@@ -41,7 +41,7 @@ def test_binding_signatures_cover_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
     assert lib.attn_status_string(OK) == b"ATTN_OK"
     assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
     assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
@@ -84,6 +84,34 @@ def test_fwd_rejects_null_misaligned_and_overlapping(lib):
     ov = list(p)
     ov[4] = ctypes.c_void_p(BASE + 3 * GAP + 16)  # lse inside o
     assert fwd(lib, ptrs=ov) == INVALID
+
+
+def fwd_fp8(lib, B=1, H=2, H_kv=2, N=128, d=128, causal=0, scale=0.125, ds=(1.0, 1.0, 1.0), ptrs=None):
+    p = ptrs or [addr(i) for i in range(5)]
+    return lib.attn_fwd_fp8(p[0], p[1], p[2], p[3], p[4], B, H, H_kv, N, d, causal, scale, *ds, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=64), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(H=3, H_kv=2), INVALID), (dict(N=0), INVALID),
+    (dict(ds=(float("nan"), 1.0, 1.0)), INVALID), (dict(ds=(1.0, float("inf"), 1.0)), INVALID),
+    (dict(ds=(1.0, 1.0, float("-inf"))), INVALID), (dict(scale=1e30, ds=(1e30, 1e30, 1.0)), INVALID),
+    (dict(scale=float("nan")), INVALID),
+])
+def test_fwd_fp8_rejects_bad_arguments(lib, kw, want):
+    assert fwd_fp8(lib, **kw) == want
+    assert lib.attn_last_error() != b""
+
+
+def test_fwd_fp8_rejects_null_misaligned_and_overlapping(lib):
+    p = [addr(i) for i in range(5)]
+    assert fwd_fp8(lib, ptrs=[None] + p[1:]) == INVALID
+    mis = list(p)
+    mis[2] = ctypes.c_void_p(BASE + 2 * GAP + 4)
+    assert fwd_fp8(lib, ptrs=mis) == INVALID
+    # o (bf16, 2 bytes per element) overlapping the end of q's uint8 range
+    ov = list(p)
+    ov[3] = ctypes.c_void_p(BASE + 2 * 128 * 128 - 16)
+    assert fwd_fp8(lib, ptrs=ov) == INVALID
 
 
 def test_fwd_varlen_validation(lib):

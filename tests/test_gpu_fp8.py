@@ -1,0 +1,211 @@
+"""Parity of the fp8 (E4M3) forward with the fp64 oracle, through the C ABI.
+
+The oracle computes exact attention of the real inputs (descale * decoded code). The tolerance is
+derived, per output element, from the two places where the kernel's arithmetic is not exact:
+
+1. The probabilities that multiply V are rounded to E4M3. Let M be the row's largest scaled score,
+   p_j = exp(s_j - M) <= 1, l = sum_j p_j, w_j = p_j / l and O_c = sum_j w_j v_jc. On chip
+   P_j = p_j * 2^(M - m + 6) with m <= M the running reference; rounding to nearest gives
+   |P~_j - P_j| <= 2^-4 P_j for normal values (three mantissa bits) and <= 2^-10 for subnormal
+   ones (spacing 2^-9). In units of p: |e_j| <= u p_j + a, u = 2^-4, a = 2^-10 / 2^6 = 2^-16.
+   The normaliser is the float32 sum of the unrounded P.
+
+2. The gfx950 E4M3 matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4) does not sum its 64
+   products exactly: measured on the device, products are summed in groups of 8 consecutive k
+   slots, and within a group each product is truncated toward zero to 14 bits below the largest
+   product of the group (so it loses less than 2^-13 of that maximum); groups and the
+   accumulator add without that loss. One instruction therefore errs by at most
+   t * sum_k |a_k b_k|, t = 2^-10. For P V that adds t * (1 + u) * sum_j w_j |v_jc|. For the
+   scores it gives |ds_j| <= delta = t * |scale| * max_j sum_d |q_d k_jd| per row, which moves
+   each softmax weight by a factor within exp(+-2 delta) and the LSE by at most delta.
+
+  Worst case per element:
+    |O~_c - O_c| <= e^(2 delta) [(u + t(1+u)) sum_j w_j|v_jc| + (a / l) sum_j |v_jc|]
+                    + (e^(2 delta) - 1) sum_j w_j|v_jc| + 2^-9 |O_c| (bf16 output)
+                    + 1e-5 sum_j w_j|v_jc| (float32 accumulation).
+  Every element must meet it. It assumes every rounding at its extreme with one sign, so a
+  second check bounds the root mean square: independent, zero-mean E4M3 roundings give
+  E[err_c^2] <= sum_j (u p_j + a)^2 v_jc^2 / l^2; the score truncations enter as a variance too
+  (at most 8 per group, each below 2^-13 of the group maximum), and the squared worst cases of the
+  P V truncation and the bf16 output rounding are added. The measured RMS over all
+  checked elements must stay below the root mean of that expectation; this is the check that sees
+  small systematic slips (a skipped tile moves every output a little).
+  |dLSE| <= delta + 2e-5 per row.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as orc
+from roofline_attention_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+U8 = 2.0 ** -4    # E4M3 relative rounding bound (round to nearest, 3 mantissa bits)
+A8 = 2.0 ** -16   # absolute rounding bound of subnormal P, relative to the row maximum
+T8 = 2.0 ** -10   # per-instruction truncation of the E4M3 matrix unit, relative to sum |a_k b_k|
+
+
+def real(t, descale):
+    return float(descale) * orc.e4m3_decode(t.numpy())
+
+
+def row_bounds(q, k, v, causal, scale, b, h, i_rows):
+    """(worst-case bound [n, d], expected squared error [n, d], LSE bound [n]) for rows i_rows of (b, h)."""
+    g = q.shape[1] // k.shape[1]
+    kh, vh = k[b, h // g], v[b, h // g]
+    i_rows = np.asarray(i_rows)
+    s = scale * (q[b, h, i_rows] @ kh.T)  # [n, N]
+    sabs = abs(scale) * (np.abs(q[b, h, i_rows]) @ np.abs(kh).T)
+    if causal:
+        keep = np.arange(kh.shape[0])[None, :] <= i_rows[:, None]
+        s = np.where(keep, s, -np.inf)
+        sabs = np.where(keep, sabs, 0.0)
+    delta = T8 * sabs.max(axis=1, keepdims=True)
+    e2 = np.exp(2 * delta)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    valid = np.isfinite(s).astype(np.float64)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ vh) / l
+    av = np.abs(vh)
+    sw = (p @ av) / l
+    worst = e2 * ((U8 + T8 * (1 + U8)) * sw + A8 * (valid @ av) / l) + (e2 - 1) * sw + 2.0 ** -9 * np.abs(o) + 1e-5 * sw
+    # score truncation as a variance: at most 8 truncations per group, each below 2^-13 of the
+    # group maximum, so E[ds^2] <= 2^-23 * scale^2 * sum_d (q_d k_d)^2; a weight then moves by
+    # w_j (ds_j - sum_i w_i ds_i), and (v_j - O) is bounded by |v_j| + |O|.
+    sq = scale ** 2 * ((q[b, h, i_rows] ** 2) @ (kh ** 2).T)
+    es2 = 2.0 ** -23 * np.where(np.isfinite(s), sq, 0.0).max(axis=1, keepdims=True)
+    w2 = (p / l) ** 2
+    ao = np.abs(o)
+    var_s = es2 * (w2 @ vh ** 2 + 2 * ao * (w2 @ av) + ao ** 2 * w2.sum(axis=1, keepdims=True))
+    var = (((U8 * p + A8 * valid) ** 2) @ (vh ** 2)) / l ** 2 + var_s + (T8 * sw) ** 2 + (2.0 ** -9 * o) ** 2
+    return worst, var, delta[:, 0] + 2e-5
+
+
+def check(o_gpu, lse_gpu, q, k, v, causal, scale, rows_by_head, ro, rl, label):
+    """rows_by_head: list of (b, h, i_rows); ro/rl: oracle values in the same order."""
+    og = I.to_f64(o_gpu)
+    errs, worsts, vars_ = [], [], []
+    gl = []
+    lse_tol = []
+    for b, h, i_rows in rows_by_head:
+        w, var, lt = row_bounds(q, k, v, causal, scale, b, h, i_rows)
+        errs.append(og[b, h, i_rows])
+        worsts.append(w)
+        vars_.append(var)
+        lse_tol.append(lt)
+        gl.append(I.to_f64(lse_gpu)[b, h, i_rows])
+    og_rows = np.concatenate(errs)
+    err = np.abs(og_rows - ro)
+    worst = np.concatenate(worsts)
+    rms, rms_bound = float(np.sqrt(np.mean(err ** 2))), float(np.sqrt(np.mean(np.concatenate(vars_))))
+    dl = np.abs(np.concatenate(gl) - rl)
+    lt = np.concatenate(lse_tol)
+    el = float(np.max(dl))
+    ratio = float(np.max(err / worst))
+    print(f"{label}: max|dO|={err.max():.3e} max(err/bound)={ratio:.3f} rms={rms:.3e} "
+          f"(model {rms_bound:.3e}) max|dLSE|={el:.3e} (bound {lt.min():.1e}..{lt.max():.1e})")
+    assert np.all(err <= worst), f"{label}: worst-case bound exceeded ({ratio:.3f})"
+    assert rms <= rms_bound, f"{label}: rms error {rms:.3e} above the rounding model {rms_bound:.3e}"
+    assert np.all(dl <= lt), f"{label}: LSE bound exceeded"
+
+
+def run(lib, t, causal, scale, descale=None):
+    descale = t["descale"] if descale is None else descale
+    o, lse = lib.fwd_fp8(t["q"].cuda(), t["k"].cuda(), t["v"].cuda(), descale, causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def full_check(lib, t, causal, scale, descale, label):
+    o, lse = run(lib, t, causal, scale, descale)
+    q, k, v = (real(t[n], s) for n, s in zip("qkv", descale))
+    ro, rl = orc.attention_fwd_fp8(t["q"].numpy(), t["k"].numpy(), t["v"].numpy(), descale, causal, scale)
+    B, H, N, _ = q.shape
+    rows = [(b, h, np.arange(N)) for b in range(B) for h in range(H)]
+    check(o, lse, q, k, v, causal, scale, rows, ro.reshape(-1, q.shape[3]), rl.reshape(-1), label)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,H_kv,N", [(1, 2, 2, 333), (2, 8, 2, 200), (1, 2, 2, 1), (1, 1, 1, 129),
+                                         (1, 2, 2, 600), (2, 4, 4, 64), (1, 4, 1, 127)])
+def test_fp8_shapes(lib, B, H, H_kv, N, causal):
+    w = I.Workload("fp8_case", "fwd", B, H, H_kv, N, 128, "e4m3", causal, seed=21)
+    t = I.make_fp8_prefill(w)
+    full_check(lib, t, causal, w.scale, t["descale"], f"fp8 B{B} H{H}/{H_kv} N{N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_arbitrary_descales_and_negative_scale(lib, causal):
+    w = I.Workload("fp8_ds", "fwd", 1, 2, 1, 300, 128, "e4m3", causal, seed=22)
+    t = I.make_fp8_prefill(w)
+    ds = (t["descale"][0] * 1.37, -t["descale"][1] * 0.81, t["descale"][2] * 0.59)
+    full_check(lib, t, causal, -0.07, ds, f"fp8 descales {ds} scale -0.07")
+
+
+def test_fp8_zero_scale_is_the_mean(lib):
+    """scale 0: every probability is 2^6 exactly, so O is the mean of V up to the matrix unit's
+    truncation (t * sum_j |v_j| / count) and the bf16 output rounding; LSE = ln(count)."""
+    w = I.Workload("fp8_zero", "fwd", 1, 2, 2, 300, 128, "e4m3", True, seed=23)
+    t = I.make_fp8_prefill(w)
+    o, lse = run(lib, t, True, 0.0)
+    v = real(t["v"], t["descale"][2])
+    count = np.arange(1, 301)[None, None, :, None]
+    mean = np.cumsum(v, axis=2) / count
+    trunc = T8 * np.cumsum(np.abs(v), axis=2) / count
+    og = I.to_f64(o)
+    err = np.abs(og - mean)
+    print(f"zero scale: max|dO|={err.max():.3e} max rel={np.max(err / np.maximum(np.abs(mean), 1e-30)):.3e} "
+          f"at {np.unravel_index(np.argmax(err - 2.0 ** -8 * np.abs(mean)), err.shape)} "
+          f"max|mean|={np.abs(mean).max():.3e}")
+    assert np.all(err <= trunc + 2.0 ** -8 * np.abs(mean) + 1e-7)
+    np.testing.assert_allclose(I.to_f64(lse), np.log(np.arange(1, 301))[None, None, :].repeat(2, 1), atol=1e-5)
+
+
+def test_fp8_causal_row0_and_one_hot_are_exact(lib):
+    w = I.Workload("fp8_row0", "fwd", 1, 2, 2, 256, 128, "e4m3", True, seed=24)
+    t = I.make_fp8_prefill(w)
+    o, _ = run(lib, t, True, w.scale)
+    v0 = torch.from_numpy(real(t["v"], t["descale"][2])[:, :, 0]).to(torch.bfloat16)  # E4M3 * 2^k fits bf16
+    assert torch.equal(o[:, :, 0], v0)
+    # one-hot: key j = unit vector e_(j mod 128) (code 0x38 = 1.0), query i = 16 * e_(i mod 128)
+    # (code 0x58), scale 4: the selected score is 64, every other is 0, so P = (2^6, 0, ...).
+    N, d = 128, 128
+    k = torch.zeros(1, 1, N, d, dtype=torch.uint8)
+    k[0, 0, torch.arange(N), torch.arange(N) % d] = 0x38
+    q = torch.zeros(1, 1, N, d, dtype=torch.uint8)
+    sel = (torch.arange(N) + 5) % d
+    q[0, 0, torch.arange(N), sel] = 0x58
+    v = t["v"][:1, :1, :N]
+    one = {"q": q, "k": k, "v": v.contiguous(), "descale": (1.0, 1.0, t["descale"][2])}
+    o1, _ = run(lib, one, False, 4.0)
+    vr = torch.from_numpy(real(one["v"], t["descale"][2])).to(torch.bfloat16)
+    assert torch.equal(o1[0, 0], vr[0, 0, sel])  # query i selects key (i + 5) mod 128 alone
+
+
+def sample_rows(B, H, N, n_rand, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [(0, 0, 0), (0, 0, 1), (B - 1, H - 1, N - 1), (0, H - 1, 127), (0, H - 1, 128), (B - 1, 0, 63),
+             (B - 1, 0, 64), (0, 1, N // 2), (B - 1, H // 2, N - 129)]
+    rnd = np.stack([rng.integers(0, B, n_rand), rng.integers(0, H, n_rand), rng.integers(0, N, n_rand)], 1)
+    return np.concatenate([np.array(fixed), rnd])
+
+
+@pytest.mark.parametrize("name", ["prefill_4k_causal_fp8", "prefill_4k_fp8"])
+def test_fp8_prefill_4k_sampled_rows_and_a_head(lib, name):
+    """The benchmarked workloads, in the benchmarked launch: 300+ sampled rows and all of head (1, 31)."""
+    w = I.WORKLOADS[name]
+    t = I.make_fp8_prefill(w)
+    o, lse = run(lib, t, w.causal, w.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    ds = t["descale"]
+    q, k, v = (real(t[n], s) for n, s in zip("qkv", ds))
+    groups = {}
+    for b, h, i in sample_rows(w.B, w.H, w.N, 300, seed=7):
+        groups.setdefault((int(b), int(h)), set()).add(int(i))
+    groups.setdefault((1, 31), set()).update(range(w.N))
+    rows_by_head = [(b, h, np.array(sorted(ii))) for (b, h), ii in sorted(groups.items())]
+    flat = np.concatenate([np.stack([np.full(len(ii), b), np.full(len(ii), h), ii], 1) for b, h, ii in rows_by_head])
+    ro, rl = orc.attention_fwd_fp8_rows(t["q"].numpy(), t["k"].numpy(), t["v"].numpy(), ds, w.causal, w.scale, flat)
+    check(o, lse, q, k, v, w.causal, w.scale, rows_by_head, ro, rl, name)
