@@ -26,6 +26,8 @@ MUTANTS = {
     "softmax_wrong_axis": ("l = e.sum(axis=1, keepdims=True)", "l = e.sum(axis=0, keepdims=True)"),
     "lse_missing_max": ("lse = (m + np.log(l))[:, 0]", "lse = (np.log(l))[:, 0]"),
     "gqa_modulo_map": ("            hk = h // g\n            s = _scores", "            hk = h % H_kv\n            s = _scores"),
+    "bwd_output_uses_unnormalised_p": ("            o[b, h] = p @ v[b, hk]\n            dv[b, hk] += p.T @ dout[b, h]",
+                                       "            o[b, h] = np.exp(s - s.max(axis=1, keepdims=True)) @ v[b, hk]\n            dv[b, hk] += p.T @ dout[b, h]"),
     "bwd_drops_D": ("ds = p * (dp - D)", "ds = p * dp"),
     "bwd_sign": ("ds = p * (dp - D)", "ds = p * (D - dp)"),
     "bwd_dk_no_scale": ("dk[b, hk] += scale * (ds.T @ q[b, h])", "dk[b, hk] += (ds.T @ q[b, h])"),
@@ -65,6 +67,7 @@ PIN_CALLS = [
     (pins.test_decode_is_last_causal_row, {}),
     (pins.test_bwd_matches_torch_autograd, dict(B=2, H=4, H_kv=2, N=23, d=8, causal=True)),
     (pins.test_bwd_sum_invariants, dict(causal=True)),
+    (pins.test_bwd_returns_the_forward, dict(causal=True)),
     (pins.test_bwd_constant_v_and_zero_scale, {}),
     (pins.test_bwd_causal_last_key, {}),
     (pins.test_varlen_equals_block_diagonal_mask, dict(causal=True, H=4, H_kv=2)),

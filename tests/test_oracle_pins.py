@@ -280,6 +280,20 @@ def test_bwd_matches_torch_autograd(B, H, H_kv, N, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_bwd_returns_the_forward(causal):
+    """attention_bwd also yields O and LSE (one pass computes forward and backward together, the
+    fused forward+backward of the MoA paper, section 4.5): pinned to torch SDPA and logsumexp."""
+    B, H, H_kv, N, d = 2, 4, 2, 29, 8
+    q, k, v, do = rand(B, H, N, d), rand(B, H_kv, N, d), rand(B, H_kv, N, d), rand(B, H, N, d)
+    _, _, _, o, lse = orc.attention_bwd(q, k, v, do, causal, 0.4)
+    np.testing.assert_allclose(o, sdpa(q, k, v, causal, 0.4), atol=1e-12)
+    s = 0.4 * torch.from_numpy(q) @ torch.from_numpy(np.repeat(k, 2, axis=1)).transpose(-1, -2)
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("H,H_kv", [(2, 2), (2, 1)])
 def test_bwd_finite_differences(causal, H, H_kv):
     N, d, scale, h = 9, 4, 0.7, 1e-6
