@@ -245,7 +245,8 @@ def main():
 
 def run_legs(torch, lib, I, L, reps=20):
     """Extra legs: the 4k prefill forward (causal and not; bf16, then fp8 inputs), the 1k causal
-    prefill, the ragged prefill, GQA decode over a contiguous and over a paged cache."""
+    prefill, the step's forward+backward as one launch, the ragged prefill, GQA decode over a
+    contiguous and over a paged cache."""
     legs = {}
     for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
         w = I.WORKLOADS[name]
@@ -285,6 +286,26 @@ def run_legs(torch, lib, I, L, reps=20):
         log(f"[bench] leg {name}: {st['avg_ms']:.3f} ms, {tf:.1f} TFLOP/s ({tf / L.PEAK_FP8_TFLOPS:.3f} of fp8 peak)")
         del t, t8, o, lse
         torch.cuda.empty_cache()
+
+    # The same forward+backward as the step, as one cooperative launch (attn_fwd_bwd)
+    w = I.WORKLOADS["fwdbwd_4k_causal"]
+    t = {k: x.cuda() for k, x in I.make_prefill(w, with_dout=True).items()}
+    outs = dict(o=torch.empty_like(t["q"]), lse=torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda"),
+                dq=torch.empty(t["q"].shape, dtype=torch.float32, device="cuda"))
+    outs["dk"], outs["dv"] = torch.empty_like(outs["dq"]), torch.empty_like(outs["dq"])
+    wsf = torch.empty(lib.fwd_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+    fn = lambda: lib.fwd_bwd(t["q"], t["k"], t["v"], t["do"], w.causal, w.scale, workspace=wsf, **outs)  # noqa
+    for _ in range(3):
+        fn()
+    wall, stats = time_region(torch, lib, fn, reps)
+    (kname, st), = stats.items()
+    fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal) + L.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    tf = fl / (st["avg_ms"] * 1e-3) / 1e12
+    legs["fwdbwd_fused"] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": tf, "frac_of_peak": tf / L.PEAK_BF16_TFLOPS,
+                            "wall_ms_per_call": wall / reps * 1e3, "launches_per_call": 1}
+    log(f"[bench] leg fwdbwd_fused: {st['avg_ms']:.3f} ms, {tf:.1f} TFLOP/s (one launch)")
+    del t, outs, wsf
+    torch.cuda.empty_cache()
 
     w = I.WORKLOADS["prefill_varlen"]
     t = I.make_varlen(w)

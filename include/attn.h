@@ -172,6 +172,27 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward and backward in ONE launch, with no atomic accumulation: the fused forward+backward of
+ * the MoA paper ("Validating Memory-Optimal Transformer Kernels on Real Hardware", sections
+ * 4.4-4.5), whose GPU version lost to the unfused pair while dK and dV were accumulated with atomics
+ * and won once every gradient element had a single owner. Computes what attn_fwd followed by
+ * attn_bwd compute (o, lse, and the gradients of L = sum(O * dO)), as one cooperative kernel: a
+ * first phase runs the forward of each query tile together with that tile's dQ, a grid barrier
+ * follows, and a second phase computes dK and dV per key tile.
+ *   q, dout [B,H,N,d], k, v [B,H_kv,N,d]: bfloat16 inputs. Outputs, fully overwritten: o [B,H,N,d]
+ *   bfloat16, lse [B,H,N] float32 (required), dq [B,H,N,d], dk, dv [B,H_kv,N,d] float32.
+ *   workspace: at least attn_fwd_bwd_workspace_size(B, H, N, d) bytes, 16-byte aligned, scratch
+ *   owned by the caller (contents need no initialisation). Calls that share a workspace must not
+ *   run concurrently.
+ * dtype must be ATTN_BF16. The launch needs the device's cooperative-launch support; it returns
+ * ATTN_ERR_HIP if the runtime refuses it.
+ */
+size_t attn_fwd_bwd_workspace_size(int B, int H, int N, int d);
+attn_status attn_fwd_bwd(const void* q, const void* k, const void* v, const void* dout, void* o, float* lse,
+                         float* dq, float* dk, float* dv, int B, int H, int H_kv, int N, int d, int causal,
+                         float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Opt-in kernel timer for measurement harnesses ("M4.2 - GPU Execution Model for Transformer
  * Kernels", section 0x0B: device-side timing with events on the launching stream). While enabled,
  * every kernel the library launches is bracketed by a pair of HIP events on its own stream.

@@ -38,6 +38,8 @@ SIGNATURES = {
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
+    "attn_fwd_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "attn_fwd_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_timing_enable": (_I, [_I]),
     "attn_timing_reset": (_I, []),
     "attn_timing_count": (_I, []),
@@ -283,6 +285,44 @@ def bwd(q, k, v, o, dout, lse, causal: bool, scale: Optional[float] = None, dq=N
                          B, H, H_kv, N, d, int(bool(causal)), float(scale), ATTN_BF16, _ptr(workspace),
                          workspace.numel(), _stream(q.device)))
     return dq, dk, dv
+
+
+def fwd_bwd_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(_lib.attn_fwd_bwd_workspace_size(B, H, N, d))
+
+
+def fwd_bwd(q, k, v, dout, causal: bool, scale: Optional[float] = None, o=None, lse=None, dq=None, dk=None,
+            dv=None, workspace: Optional[torch.Tensor] = None):
+    """Forward and backward in one launch: bf16 q, dout [B,H,N,d], k, v [B,H_kv,N,d].
+
+    Returns (o bf16 [B,H,N,d], lse fp32 [B,H,N], dq fp32 [B,H,N,d], dk, dv fp32 [B,H_kv,N,d])."""
+    _need(q, "q", torch.bfloat16)
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, (B, H_kv, N, d), q.device)
+    _need(dout, "dout", torch.bfloat16, q.shape, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if o is None else o
+    lse = torch.empty((B, H, N), **f32) if lse is None else lse
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(k.shape, **f32) if dk is None else dk
+    dv = torch.empty(v.shape, **f32) if dv is None else dv
+    _need(o, "o", torch.bfloat16, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    _need(dq, "dq", torch.float32, q.shape, q.device)
+    _need(dk, "dk", torch.float32, k.shape, q.device)
+    _need(dv, "dv", torch.float32, v.shape, q.device)
+    need = fwd_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(_lib.attn_fwd_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(o), _ptr(lse), _ptr(dq), _ptr(dk),
+                             _ptr(dv), B, H, H_kv, N, d, int(bool(causal)), float(scale), ATTN_BF16,
+                             _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return o, lse, dq, dk, dv
 
 
 def timing_enable(on: bool = True) -> None:

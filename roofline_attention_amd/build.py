@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libroofattn.so")
-SOURCES = ["attn_api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["attn_api.hip", "fwd_bf16.hip", "fwd_fp8.hip", "fwd_f32.hip", "decode.hip", "bwd.hip", "fused.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every HIP translation unit.
 HIPFLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -131,7 +131,7 @@ TimedScope::~TimedScope() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 4; }
+int attn_abi_version(void) { return 5; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -339,6 +339,43 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
       if (overlap(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
   return hip_status(ra::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal != 0, scale, workspace,
                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_fwd_bwd_workspace_size(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  return ra::fwdbwd_workspace_bytes(B, H, N, d);
+}
+
+attn_status attn_fwd_bwd(const void* q, const void* k, const void* v, const void* dout, void* o, float* lse,
+                         float* dq, float* dk, float* dv, int B, int H, int H_kv, int N, int d, int causal,
+                         float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !dout || !o || !lse || !dq || !dk || !dv)
+    return fail(ATTN_ERR_INVALID_ARG, "all tensor pointers must be non-null");
+  attn_status st = check_shape(B, H, H_kv, N, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the fused forward+backward supports ATTN_BF16 only");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(ATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t need = ra::fwdbwd_workspace_bytes(B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "fused forward+backward workspace too small");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const long long tiles = (long long)((N + 127) / 128) * H * B;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  const size_t tb = (size_t)B * H * N * d * 2, kb = (size_t)B * H_kv * N * d * 2, gb = (size_t)B * H * N * d * 4,
+               gkb = (size_t)B * H_kv * N * d * 4, lb = (size_t)B * H * N * 4;
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}, {dout, tb}};
+  const Range outs[] = {{o, tb}, {lse, lb}, {dq, gb}, {dk, gkb}, {dv, gkb}, {workspace, need}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
+  return hip_status(ra::launch_fwd_bwd(q, k, v, dout, o, lse, dq, dk, dv, B, H, H_kv, N, d, causal != 0, scale,
+                                       workspace, static_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_timing_enable(int on) {

@@ -25,32 +25,11 @@
 // tile, so nothing is transposed in memory. Tiles reach LDS by direct buffer loads whose range
 // check zero-fills rows past the sequence end; zero Q/dO rows and zero K/V rows contribute
 // nothing to any stored gradient, so only the causal diagonal needs a mask.
-#include <math.h>
-
-#include <type_traits>
-
-#include "common.hpp"
+#include "bwd_job.hpp"
 #include "kernels.hpp"
-#include "lds_tile.hpp"
 
 namespace ra {
 namespace {
-
-constexpr int BWD_THREADS = 256;
-// Waves per SIMD the register budget is sized for. The key-major kernel holds K, V operands and
-// fp32 dK, dV accumulators (about 330 registers): one wave per SIMD keeps the accumulators in
-// AGPRs without spilling, which measured faster than two spilling waves.
-#ifndef RA_DKDV_WAVES_PER_SIMD
-#define RA_DKDV_WAVES_PER_SIMD 1
-#endif
-#ifndef RA_DKDV_PAIR
-#define RA_DKDV_PAIR 0
-#endif
-#ifndef RA_DQ_WAVES_PER_SIMD
-#define RA_DQ_WAVES_PER_SIMD 2
-#endif
-constexpr int BWD_BQ = 64;   // queries per staged tile in the key-major kernel
-constexpr int BWD_BK = 64;   // keys per staged tile in the query-major kernel
 
 // ------------------------------------------------------------------------- preprocess ----
 
@@ -81,61 +60,6 @@ __global__ __launch_bounds__(BWD_THREADS) void bwd_pre_kernel(const bf16* __rest
     L2[row] = LSE[row] * kLog2e;  // the row's LSE in log2 units, streamed by the key-major kernel
   }
 }
-
-// Per-lane constants of the transposed read over a [rows][HD] tile with swizzle SWZ: in its
-// 16-lane group, source lane 4e + j points at row (4g + e) of an 8-row-aligned block and element
-// column 16 * ((lane / 16) % 2) + 4j of a 32-column block. The swizzle of that row depends on the
-// block's row base only through its bit 3 (the second half of a 16-row k-step), so two lane
-// constants cover both halves. Returns the element offset for (row base rb, column block cb).
-template <int HD, int (*SWZ)(int)>
-struct TrLane {
-  int row_off;  // (4g + e) * HD + 4 * (j & 1)
-  int t0, t8;   // chunk XOR constants for row bases = 0 and = 8 (mod 16)
-  __device__ __forceinline__ TrLane(int lane) {
-    const int g = lane >> 5;
-    const int e = (lane & 15) >> 2;
-    const int x = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    row_off = (4 * g + e) * HD + 4 * (lane & 1);
-    t0 = x ^ SWZ(4 * g + e);
-    t8 = x ^ SWZ(8 + 4 * g + e);
-  }
-  // element offset of this lane's 4 x bf16 for rows rb + (4g + e), 32-column block cb
-  __device__ __forceinline__ int at(int rb, int cb) const {
-    return rb * HD + row_off + ((4 * cb) ^ ((rb & 8) ? t8 : t0)) * 8;
-  }
-};
-
-template <int HD>
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, const TrLane<HD, swz_both<HD>>& tl, int rb, int cb) {
-  return __builtin_shufflevector(lds_read_tr(tile + tl.at(rb, cb)), lds_read_tr(tile + tl.at(rb + 8, cb)), 0, 1, 2,
-                                 3, 4, 5, 6, 7);
-}
-
-// ------------------------------------------------------------------------------ dK dV ----
-
-constexpr int DKDV_STAGES = 3;  // query tiles resident in LDS: one read, one in flight, one draining
-
-template <int HD>
-struct DkdvSmem {
-  bf16 q[DKDV_STAGES][BWD_BQ * HD];
-  bf16 dO[DKDV_STAGES][BWD_BQ * HD];
-  float lse[DKDV_STAGES][BWD_BQ];
-  float dd[DKDV_STAGES][BWD_BQ];
-};
-
-// Work is cut into 32-query blocks u (block u = query rows 32u .. 32u + 31, half u % 2 of query
-// tile u / 2), each in three parts:
-//   A(u): S and dP accumulators for the wave's 32 keys (16 MFMAs on row operands of the tile),
-//   V(u): P = 2^(S c - LSE log2 e) and dS = P (dP - D), rounded to bf16 (vector ALUs),
-//   B(u): dV += P^T dO and dK += dS^T Q (16 MFMAs on transposed operands of the tile).
-// A step issues A(u+1), V(u) and B(u-1): three independent chains that the wave interleaves. (On
-// gfx950 a vector instruction overlaps a running MFMA only when both come from the same wave, so
-// the exponentials of one block must sit between the MFMAs of its neighbours.) Query tiles rotate
-// through three LDS stages: tile t is read from step 2t-1 (by A) to step 2t+2 (by B), and tile t+2
-// is loaded into the stage of tile t-1 right after the barrier between tile t's two steps.
-// Causal workgroups run their first two query tiles (the ones crossing the diagonal of some wave)
-// block by block with the mask, and the pipeline from the third tile on, where no key of the
-// workgroup follows any query.
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -143,207 +67,9 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
     float* __restrict__ dK, float* __restrict__ dV, int H, int group, int N, int n_ktiles, float scale,
     float scale_log2) {
   extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
-  DkdvSmem<HD>& sm = *reinterpret_cast<DkdvSmem<HD>*>(dyn_smem);
-  constexpr int KSTEPS = HD / 16;
-  constexpr int CBLK = HD / 32;
-
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  constexpr bool PAIR = CAUSAL && RA_DKDV_PAIR;
-  const int per = PAIR ? (n_ktiles + 1) / 2 : n_ktiles;  // workgroups per (sequence, KV head)
-  const int pair = item % per;
-  const int bhk = item / per;  // (sequence, KV head)
-  const int Hkv = H / group;
-  const int b = bhk / Hkv;
-  const int hk = bhk % Hkv;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  // With RA_DKDV_PAIR a causal workgroup takes the key tiles (p, n - 1 - p) one after the other so
-  // every workgroup carries the same work (as the forward and dQ do). For this kernel, at one
-  // workgroup per CU, it measured slower at N >= 4096 (4096: 454 vs 417 us, 8192: 853 vs 735 us)
-  // and faster only at 1024, so the default keeps one key tile per workgroup, heaviest first.
-  for (int rep = 0; rep < (PAIR ? 2 : 1); ++rep) {
-    const int kt = PAIR && rep == 1 ? n_ktiles - 1 - pair : pair;
-    if (rep == 1 && kt == pair) break;  // odd tile count: the middle tile runs once
-    // every wave is done with the first tile's LDS stages
-    if (rep == 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const size_t head = (size_t)bhk * N * HD;  // K, V, dK, dV rows of this KV head
-    const int kw0 = kt * 128 + w * 32;  // this wave's first key
-    const int key = kw0 + l32;          // the key column this lane holds in S and dP
-
-    bf16x8 kf[KSTEPS], vf[KSTEPS];
-    if (key < N) {
-      const bf16x8* ks = reinterpret_cast<const bf16x8*>(K + head + (size_t)key * HD);
-      const bf16x8* vs = reinterpret_cast<const bf16x8*>(V + head + (size_t)key * HD);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        kf[kk] = ks[2 * kk + g];
-        vf[kk] = vs[2 * kk + g];
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) kf[kk] = vf[kk] = bf16x8{};
-    }
-
-    f32x16 dk[CBLK], dv[CBLK];
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) dk[cb] = dv[cb] = f32x16{};
-
-    const TrLane<HD, swz_both<HD>> tl(lane);
-    // Row-operand reads (A = Q or dO rows of a 32-query block): row qb*32 + l32, chunk 2kk + g.
-    const int row_t = g ^ swz_both<HD>(l32);  // swz_both repeats every 16 rows
-    const int row_off = l32 * HD;
-    // Query-side rows of the query head currently streamed (set per head of the group below).
-    const bf16* Qh = nullptr;
-    const bf16* dOh = nullptr;
-    const float* LSEh = nullptr;
-    const float* Dh = nullptr;
-    const int n_qt = (N + BWD_BQ - 1) / BWD_BQ;
-
-    auto stage_of = [](int t) { return (t + DKDV_STAGES) % DKDV_STAGES; };  // t >= -1
-    auto stage = [&](int qt) {
-      const int s = stage_of(qt);
-      const int r0 = qt * BWD_BQ;
-      stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(Qh, r0, N, sm.q[s], w, lane);
-      stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(dOh, r0, N, sm.dO[s], w, lane);
-      if (w == 0) load_to_lds<4>(dma_rsrc(LSEh + r0, (N - r0) * 4), lane * 4, sm.lse[s]);
-      if (w == 1) load_to_lds<4>(dma_rsrc(Dh + r0, (N - r0) * 4), lane * 4, sm.dd[s]);
-    };
-    // Barrier between the two steps of tile t: this wave's loads of tile t+1 have landed and every
-    // wave's reads of tile t-1 have returned; then tile t+2 goes into tile t-1's stage.
-    auto mid = [&](int t) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (t + 2 < n_qt) stage(t + 2);
-    };
-
-    auto blk_A = [&](int u, f32x16& sacc, f32x16& dpacc) {
-      const int s = stage_of(u >> 1);
-      const bf16* qrow = sm.q[s] + (u & 1) * 32 * HD + row_off;
-      const bf16* drow = sm.dO[s] + (u & 1) * 32 * HD + row_off;
-      sacc = f32x16{};
-      dpacc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const int off = ((2 * kk) ^ row_t) * 8;
-        sacc = mfma32(*reinterpret_cast<const bf16x8*>(qrow + off), kf[kk], sacc);
-        dpacc = mfma32(*reinterpret_cast<const bf16x8*>(drow + off), vf[kk], dpacc);
-      }
-    };
-    // S, dP lanes: column = key, rows = queries 32u + 8(r/4) + 4g + r%4. P^T and dS^T leave in the
-    // A-operand layout of B (lane row = key, k-step hh covers queries 16hh + {4g..4g+3, 8+4g..}).
-    auto blk_V = [&](int u, const f32x16& sacc, const f32x16& dpacc, bf16x8 (&pb)[2], bf16x8 (&dsb)[2],
-                     bool mask) {
-      const int s = stage_of(u >> 1);
-      const int qb = u & 1;
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[s][qb * 32 + 8 * rg + 4 * g]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[s][qb * 32 + 8 * rg + 4 * g]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rg + e;
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e]));  // l4: LSE * log2 e
-          if (mask && key > 32 * u + 8 * rg + 4 * g + e) p = 0.f;
-          pb[r >> 3][r & 7] = to_bf16(p);
-          dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - d4[e]));
-        }
-      }
-    };
-    // B operands: dO / Q columns 32cb + l32 by transposed read.
-    auto blk_B = [&](int u, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
-      const int s = stage_of(u >> 1);
-      const int r0 = (u & 1) * 32;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) {
-          dv[cb] = mfma32(pb[hh], tr_operand<HD>(sm.dO[s], tl, r0 + 16 * hh, cb), dv[cb]);
-          dk[cb] = mfma32(dsb[hh], tr_operand<HD>(sm.q[s], tl, r0 + 16 * hh, cb), dk[cb]);
-        }
-      }
-    };
-
-    // The group's query heads run one after another over the same K/V rows; dK and dV accumulate
-    // across them in registers, so each element is still written once.
-    for (int j = 0; j < group; ++j) {
-      const size_t qrows = (size_t)b * H + (size_t)hk * group + j;
-      Qh = Q + qrows * N * HD;
-      dOh = dO + qrows * N * HD;
-      LSEh = LSE2 + qrows * N;  // LSE * log2 e, from the preprocess
-      Dh = Dg + qrows * N;
-      // Every wave has finished reading the previous head's tiles before this head's prologue
-      // writes LDS.
-      if (j > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      const int t_first = CAUSAL ? (kt * 128) / BWD_BQ : 0;
-      if (!CAUSAL) {
-        // The pipeline's first step applies B to block -1 with zero P and dS; its stage must hold
-        // finite values (0 * NaN would poison the accumulators).
-        const int s = stage_of(-1);
-        bf16x8* zq = reinterpret_cast<bf16x8*>(sm.q[s]);
-        bf16x8* zd = reinterpret_cast<bf16x8*>(sm.dO[s]);
-        for (int i = tid; i < BWD_BQ * HD / 8; i += BWD_THREADS) zq[i] = zd[i] = bf16x8{};
-      }
-      stage(t_first);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (t_first + 1 < n_qt) stage(t_first + 1);
-
-      int t = t_first;
-      if (CAUSAL) {
-        for (; t < min(n_qt, t_first + 2); ++t) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            if (h == 1) mid(t);
-            f32x16 sacc, dpacc;
-            bf16x8 pb[2], dsb[2];
-            blk_A(2 * t + h, sacc, dpacc);
-            blk_V(2 * t + h, sacc, dpacc, pb, dsb, true);
-            blk_B(2 * t + h, pb, dsb);
-          }
-        }
-      }
-      if (t < n_qt) {
-        f32x16 sa, da, sb, db;
-        bf16x8 pc[2], dc[2], pp[2], dpp[2];
-        pp[0] = pp[1] = dpp[0] = dpp[1] = bf16x8{};
-        blk_A(2 * t, sa, da);
-        for (; t < n_qt; ++t) {
-          blk_A(2 * t + 1, sb, db);
-          blk_V(2 * t, sa, da, pc, dc, false);
-          blk_B(2 * t - 1, pp, dpp);
-          mid(t);
-          blk_A(2 * t + 2, sa, da);  // past the last tile this reads a drained stage; the result is unused
-          blk_V(2 * t + 1, sb, db, pp, dpp, false);
-          blk_B(2 * t, pc, dc);
-        }
-        blk_B(2 * n_qt - 1, pp, dpp);
-      }
-    }
-
-    // dK/dV accumulators: lane column c = 32cb + l32, rows = keys kw0 + 8(r/4) + 4g + r%4.
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (kr < N) {
-          dK[head + (size_t)kr * HD + 32 * cb + l32] = dk[cb][r] * scale;
-          dV[head + (size_t)kr * HD + 32 * cb + l32] = dv[cb][r];
-        }
-      }
-    }
-  }
+  bwd_dkdv_job<HD, CAUSAL>(Q, K, V, dO, LSE2, Dg, dK, dV, H, group, N, n_ktiles, scale, scale_log2,
+                           *reinterpret_cast<DkdvSmem<HD>*>(dyn_smem), xcd_remap(blockIdx.x, gridDim.x));
 }
-
-// --------------------------------------------------------------------------------- dQ ----
-
-template <int HD>
-struct DqSmem {
-  bf16 k[2][BWD_BK * HD];
-  bf16 v[2][BWD_BK * HD];
-};
 
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kernel(
@@ -351,126 +77,8 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
     float* __restrict__ dQ, int H, int group, int N, int n_qtiles, float scale, float scale_log2) {
   __shared__ DqSmem<HD> sm;
-  constexpr int KSTEPS = HD / 16;
-  constexpr int CBLK = HD / 32;
-
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int per = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;  // workgroups per (sequence, head)
-  const int pair = item % per;
-  const int bh = item / per;
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  // Causal work per query tile grows with its index: a causal workgroup takes the query tiles
-  // (n - 1 - p, p) one after the other and every workgroup carries the same work.
-  for (int rep = 0; rep < (CAUSAL ? 2 : 1); ++rep) {
-    const int qt = CAUSAL && rep == 0 ? n_qtiles - 1 - pair : pair;
-    if (rep == 1 && qt == n_qtiles - 1 - pair) break;  // odd tile count: the middle tile runs once
-    // every wave is done with the first tile's LDS stages
-    if (rep == 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const size_t head = (size_t)bh * N * HD;  // Q, dO, dQ rows of this query head
-    const size_t rowbase = (size_t)bh * N;
-    const size_t kv_head = ((size_t)(bh / H) * (H / group) + (bh % H) / group) * N * HD;
-    const int q0 = qt * 128 + w * 32;
-    const int qi = q0 + l32;
-
-    bf16x8 qf[KSTEPS], df[KSTEPS];
-    float lse2 = 0.f, Dq = 0.f;  // rows past N: Q = dO = 0 gives dS = 0
-    if (qi < N) {
-      const bf16x8* qs = reinterpret_cast<const bf16x8*>(Q + head + (size_t)qi * HD);
-      const bf16x8* ds = reinterpret_cast<const bf16x8*>(dO + head + (size_t)qi * HD);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        qf[kk] = qs[2 * kk + g];
-        df[kk] = ds[2 * kk + g];
-      }
-      lse2 = LSE[rowbase + qi] * kLog2e;
-      Dq = Dg[rowbase + qi];
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = df[kk] = bf16x8{};
-    }
-
-    f32x16 acc[CBLK];
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) acc[cb] = f32x16{};
-
-    const TrLane<HD, swz_both<HD>> tl(lane);
-    const int krow_t = g ^ swz_both<HD>(l32);
-    const int vrow_t = g ^ swz_rows<HD>(l32);
-    const int row_off = l32 * HD;
-    const bf16* Kh = K + kv_head;
-    const bf16* Vh = V + kv_head;
-
-    auto stage = [&](int t, int s) {
-      stage_tile<HD, BWD_BK, 4, swz_both<HD>>(Kh, t * BWD_BK, N, sm.k[s], w, lane);
-      stage_tile<HD, BWD_BK, 4, swz_rows<HD>>(Vh, t * BWD_BK, N, sm.v[s], w, lane);
-    };
-
-    const int q_end = min(N, qt * 128 + 128);
-    const int n_kt = CAUSAL ? (q_end + BWD_BK - 1) / BWD_BK : (N + BWD_BK - 1) / BWD_BK;
-    // One key tile from LDS stage s; MASK applies the causal mask, needed only on the last two key
-    // tiles: every key of a tile below them precedes the workgroup's first query (n_kt - 2 <= 2 qt).
-    auto tile = [&](int s, int t, auto MASK_) {
-      constexpr bool MASK = decltype(MASK_)::value;
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 1 < n_kt) stage(t + 1, 1 - s);
-      const int k0 = t * BWD_BK;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        // S^T and dP^T: lane column = query, rows = keys k0 + 32kb + 8(r/4) + 4g + r%4. The first
-        // k-step takes a zero accumulator operand directly (no zero-filled registers).
-        const bf16* krow = sm.k[s] + kb * 32 * HD + row_off;
-        const bf16* vrow = sm.v[s] + kb * 32 * HD + row_off;
-        f32x16 sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + (0 ^ krow_t) * 8), qf[0], f32x16{});
-        f32x16 dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + (0 ^ vrow_t) * 8), df[0], f32x16{});
-#pragma unroll
-        for (int kk = 1; kk < KSTEPS; ++kk) {
-          sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ krow_t) * 8), qf[kk], sacc);
-          dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + ((2 * kk) ^ vrow_t) * 8), df[kk], dpacc);
-        }
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[r], scale_log2, -lse2));
-          if (MASK && k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) > qi) p = 0.f;
-          dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - Dq));
-        }
-        // dQ^T += K^T dS^T for this block's 32 keys: A = K^T (rows c = 32cb + l32 by transposed
-        // read of the key tile), k-steps 2kb, 2kb + 1.
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int cb = 0; cb < CBLK; ++cb)
-            acc[cb] = mfma32(tr_operand<HD>(sm.k[s], tl, 32 * kb + 16 * hh, cb), dsb[hh], acc[cb]);
-        }
-      }
-    };
-    using NoMask = std::integral_constant<bool, false>;
-    using Mask = std::integral_constant<bool, true>;
-    const int t_mask = CAUSAL ? max(0, n_kt - 2) : n_kt;
-    stage(0, 0);
-    int t = 0;
-    for (; t < t_mask; ++t) tile(t & 1, t, NoMask{});
-    for (; t < n_kt; ++t) tile(t & 1, t, Mask{});
-
-    if (qi < N) {
-      float* out = dQ + head + (size_t)qi * HD;
-#pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * rg + 4 * g) =
-              f32x4{acc[cb][4 * rg] * scale, acc[cb][4 * rg + 1] * scale, acc[cb][4 * rg + 2] * scale,
-                    acc[cb][4 * rg + 3] * scale};
-        }
-      }
-    }
-  }
+  bwd_dq_job<HD, CAUSAL>(Q, K, V, dO, LSE, Dg, dQ, H, group, N, n_qtiles, scale, scale_log2, sm,
+                         xcd_remap(blockIdx.x, gridDim.x));
 }
 
 template <int HD, bool CAUSAL>

@@ -65,4 +65,11 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       int B, int H, int H_kv, int N, int d, bool causal, float scale, void* ws,
                       hipStream_t stream);
 
+// Forward and backward in one cooperative launch: o, lse from the forward and dq, dk, dv from the
+// backward, with the workspace holding D, LSE * log2 e and an item counter.
+size_t fwdbwd_workspace_bytes(int B, int H, int N, int d);
+hipError_t launch_fwd_bwd(const void* q, const void* k, const void* v, const void* dout, void* o, float* lse,
+                          float* dq, float* dk, float* dv, int B, int H, int H_kv, int N, int d, bool causal,
+                          float scale, void* ws, hipStream_t stream);
+
 }  // namespace ra

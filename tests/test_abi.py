@@ -41,7 +41,7 @@ def test_binding_signatures_cover_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 4
+    assert lib.attn_abi_version() == 5
     assert lib.attn_status_string(OK) == b"ATTN_OK"
     assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
     assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
@@ -186,6 +186,25 @@ def test_bwd_validation(lib):
     assert call(H_kv=5) == INVALID  # 16 query heads do not split into 5 groups
     assert call(dtype=F32) == UNSUPPORTED
     assert call(lse=None) == INVALID
+
+
+def test_fwd_bwd_validation(lib):
+    p = [addr(i) for i in range(10)]
+    ws_need = lib.attn_fwd_bwd_workspace_size(1, 2, 128, 64)
+    assert ws_need == 2 * 2 * 128 * 4 + 16
+    assert lib.attn_fwd_bwd_workspace_size(1, 2, 128, 96) == 0
+
+    def call(B=1, H=2, H_kv=2, N=128, d=64, dtype=BF16, ws_bytes=ws_need, ptrs=p):
+        return lib.attn_fwd_bwd(*ptrs[:9], B, H, H_kv, N, d, 1, 0.125, dtype, ptrs[9], ws_bytes, None)
+
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
+    assert call(H=3) == INVALID
+    assert call(ws_bytes=ws_need - 1) == WORKSPACE
+    assert call(ptrs=p[:5] + [None] + p[6:]) == INVALID  # lse is required
+    ov = list(p)
+    ov[6] = p[0]  # dq on top of q
+    assert call(ptrs=ov) == INVALID
 
 
 def test_timer_without_launches(lib):
