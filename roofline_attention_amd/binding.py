@@ -19,6 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("ROOFATTN_LIB", os.path.join(_HERE, "libroofattn.so"))
 
 ATTN_F32, ATTN_BF16 = 0, 1
+# The ABI version these signatures describe (attn_abi_version() of the matching library).
+ABI_VERSION = 5
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 # Every symbol include/attn.h declares, with (restype, argtypes).
@@ -60,6 +62,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.attn_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} reports ABI version {lib.attn_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}: rebuild the library from these sources")
     return lib
 
 
