@@ -136,7 +136,7 @@ def cpu_baseline(w, target_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build runs on a single "
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this library runs on a single "
               f"MI355X and has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
