@@ -78,4 +78,17 @@ __device__ __forceinline__ int xcd_remap(int L, int total) {
   return (L % kXcd) * per + L / kXcd;
 }
 
+// Items that share data come in groups of `ipg` consecutive indices (e.g. the query heads and
+// tiles of one KV head of one sequence). Workgroup slot L runs on XCD L % 8; this mapping gives XCD
+// x the groups x, x + 8, x + 16, ..., so every XCD receives the same share of every sequence
+// whatever the sequences' lengths, while a group stays on one XCD's L2. (A contiguous split of
+// the item range, as xcd_remap makes, hands whole sequences to single XCDs.)
+__device__ __forceinline__ int xcd_group_remap(int L, int total, int ipg) {
+  constexpr int kXcd = 8;
+  if (ipg <= 0 || total % ipg != 0 || (total / ipg) % kXcd != 0) return L;
+  const int x = L % kXcd;
+  const int j = L / kXcd;
+  return ((j / ipg) * kXcd + x) * ipg + j % ipg;
+}
+
 }  // namespace ra

@@ -11,8 +11,14 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ cu_seqlens, int T, int H,
     int group, int N, int n_qtiles, float scale_log2) {
+  // A ragged batch deals the KV-head groups of its sequences round-robin over the XCDs (sequence
+  // lengths differ, so a contiguous split would load the XCDs unevenly); a dense batch keeps
+  // consecutive items (one head's tiles) together on an XCD.
+  const int per_head = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  const int item = VARLEN ? xcd_group_remap(blockIdx.x, gridDim.x, group * per_head)
+                          : xcd_remap(blockIdx.x, gridDim.x);
   fwd_bf16_job<HD, CAUSAL, VARLEN, false>(Q, K, V, O, LSE, cu_seqlens, T, H, group, N, n_qtiles, scale_log2,
-                                          nullptr, xcd_remap(blockIdx.x, gridDim.x), nullptr, nullptr, nullptr);
+                                          nullptr, item, nullptr, nullptr, nullptr);
 }
 
 template <int HD, bool CAUSAL, bool VARLEN>

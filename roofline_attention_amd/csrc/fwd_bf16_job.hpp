@@ -133,10 +133,15 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
   }
   // Causal work per query tile grows with its index, so a causal workgroup takes the pair of tiles
   // (n - 1 - p, p): every workgroup then does the same work and the last round has no long tail
-  // (measured: 75% of workgroup slots busy with one tile per workgroup, heaviest first).
+  // (measured: 75% of workgroup slots busy with one tile per workgroup, heaviest first). n counts
+  // the tiles of this workgroup's own sequence: in a ragged batch the grid covers the longest one,
+  // and pairing a shorter sequence against that count would give a few workgroups all its heavy
+  // tiles (measured: twice the time of the ragged workload).
+  const int n_own = VARLEN ? (Nb + FWD_BR - 1) / FWD_BR : n_qtiles;
+  if (CAUSAL && pair >= (n_own + 1) / 2) return;  // no tile of this sequence left for this pair slot
   for (int rep = 0; rep < (CAUSAL ? 2 : 1); ++rep) {
-    const int qt = CAUSAL && rep == 0 ? n_qtiles - 1 - pair : pair;
-    if (rep == 1 && qt == n_qtiles - 1 - pair) break;  // odd tile count: the middle tile runs once
+    const int qt = CAUSAL && rep == 0 ? n_own - 1 - pair : pair;
+    if (rep == 1 && qt == n_own - 1 - pair) break;  // odd tile count: the middle tile runs once
     if (qt * FWD_BR >= Nb) continue;  // query tile past this sequence (uniform over the workgroup)
     if (rep == 1) __syncthreads();     // every wave is done with the first tile's LDS stages
     const int q0 = qt * FWD_BR + w * 32;
