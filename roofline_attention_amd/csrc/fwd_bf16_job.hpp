@@ -86,7 +86,8 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
                                              float* __restrict__ LSE, const int32_t* __restrict__ cu_seqlens,
                                              int T, int H, int group, int N, int n_qtiles, float scale_log2,
                                              FwdSmem<HD>* ext, int item, const bf16* __restrict__ dO,
-                                             float* __restrict__ Dg, float* __restrict__ L2) {
+                                             float* __restrict__ Dg, float* __restrict__ L2,
+                                             int only_rep = -1) {
   __shared__ FwdSmem<HD> own;  // unreferenced, hence not allocated, when FUSED
   FwdSmem<HD>& sm = FUSED ? *ext : own;
   constexpr int KSTEPS = HD / 16;  // MFMA k-steps over the head dimension
@@ -137,13 +138,15 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
   // the tiles of this workgroup's own sequence: in a ragged batch the grid covers the longest one,
   // and pairing a shorter sequence against that count would give a few workgroups all its heavy
   // tiles (measured: twice the time of the ragged workload).
+  // only_rep 0 or 1 runs just the heavy or just the light tile of the pair (a small grid then
+  // launches each pair as two workgroups, filling twice the workgroup slots); -1 runs both.
   const int n_own = VARLEN ? (Nb + FWD_BR - 1) / FWD_BR : n_qtiles;
   if (CAUSAL && pair >= (n_own + 1) / 2) return;  // no tile of this sequence left for this pair slot
-  for (int rep = 0; rep < (CAUSAL ? 2 : 1); ++rep) {
+  for (int rep = (only_rep == 1 ? 1 : 0); rep < (CAUSAL && only_rep != 0 ? 2 : 1); ++rep) {
     const int qt = CAUSAL && rep == 0 ? n_own - 1 - pair : pair;
     if (rep == 1 && qt == n_own - 1 - pair) break;  // odd tile count: the middle tile runs once
     if (qt * FWD_BR >= Nb) continue;  // query tile past this sequence (uniform over the workgroup)
-    if (rep == 1) __syncthreads();     // every wave is done with the first tile's LDS stages
+    if (rep == 1 && only_rep < 0) __syncthreads();  // every wave is done with the first tile's LDS stages
     const int q0 = qt * FWD_BR + w * 32;
     const int qi = q0 + l32;
 
