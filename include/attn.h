@@ -80,7 +80,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  *   real Q = q_descale * decode(q), real K = k_descale * decode(k), real V = v_descale * decode(v),
  *   O = softmax(scale * Q K^T [causal]) V of those real values, LSE as for attn_fwd.
  *   q [B, H, N, d], k, v [B, H_kv, N, d]: uint8 codes; o [B, H, N, d] bfloat16 (nearest even);
- *   lse [B, H, N] float32 or NULL. d must be 128. Descales must be finite (any sign or zero).
+ *   lse [B, H, N] float32 or NULL. d must be 64 or 128. Descales must be finite (any sign or zero).
  * Accuracy: scores are exact products of the codes accumulated in float32; the probabilities that
  * multiply V are rounded to E4M3 (relative error at most 2^-4 each, values below 2^-12 of the row
  * maximum with an absolute error of at most 2^-16 of it), while the normaliser and LSE use the

@@ -177,7 +177,6 @@ attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, f
   if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   attn_status st = check_shape(B, H, H_kv, N, d, scale);
   if (st != ATTN_OK) return st;
-  if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "the fp8 forward supports d = 128 only");
   if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale))
     return fail(ATTN_ERR_INVALID_ARG, "descale factors must be finite");
   if (!(fabs((double)scale * q_descale * k_descale * 1.4426950408889634) <= (double)FLT_MAX))
@@ -192,7 +191,7 @@ attn_status attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, f
     return fail(ATTN_ERR_INVALID_ARG, "outputs overlap inputs or each other");
   const long long tiles = (long long)((N + 127) / 128) * H * B;
   if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
-  return hip_status(ra::launch_fwd_fp8(q, k, v, o, lse, B, H, H_kv, N, causal != 0, scale, q_descale, k_descale,
+  return hip_status(ra::launch_fwd_fp8(q, k, v, o, lse, B, H, H_kv, N, d, causal != 0, scale, q_descale, k_descale,
                                        v_descale, static_cast<hipStream_t>(stream)));
 }
 

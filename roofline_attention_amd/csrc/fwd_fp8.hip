@@ -1,4 +1,4 @@
-// Fused tiled attention forward for fp8 (OCP E4M3) inputs on gfx950, d = 128.
+// Fused tiled attention forward for fp8 (OCP E4M3) inputs on gfx950, d = 64 or 128.
 //
 // Same schedule as the bf16 forward ("Why Fast GPUs Still Wait for Memory", section
 // "FlashAttention is an IO algorithm"): a workgroup owns 128 query rows of one (batch, head),
@@ -17,7 +17,7 @@
 //   * V^T comes from ds_read_b64_tr_b8: in each 16-lane group, source lane 2k + b supplies key row
 //     k of the read and byte column 8b .. 8b+7, and result lane t receives column t of those 8
 //     keys. Four such reads give the 32 keys of a lane in the order of its probabilities.
-//   * K and V tiles (128-byte rows) go straight from HBM into LDS, 16-byte chunks XOR-swizzled so
+//   * K and V tiles (d-byte rows) go straight from HBM into LDS, 16-byte chunks XOR-swizzled so
 //     that the K row reads (16 rows per b128 phase) and the transposed V reads (8 rows x 2 chunks
 //     per 32 lanes) hit distinct banks.
 //   * P is formed as 2^(s - m + 6) with the running maximum m raised only when a tile's maximum
@@ -41,21 +41,31 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 constexpr int F8_BR = 128;
 constexpr int F8_BC = 64;
 constexpr int F8_THREADS = 256;
-constexpr int F8_HD = 128;          // head dimension = bytes per K/V row
 constexpr float kLazy = 2.0f;       // log2 units
 constexpr float kPOffset = 6.0f;    // log2 of the factor P carries while on chip
 
-struct Fp8Smem {
-  uint8_t k[2][F8_BC * F8_HD];
-  uint8_t v[2][F8_BC * F8_HD];
+template <int HD>
+struct Fp8Smem {  // HD = head dimension = bytes per K/V row
+  uint8_t k[2][F8_BC * HD];
+  uint8_t v[2][F8_BC * HD];
 };
 
-// Chunk swizzles of 128-byte rows (8 chunks of 16 bytes; rows alternate between the two halves of
-// the 64 banks by parity). K: a b128 phase reads chunk c of 16 consecutive rows, so the 8 rows of
-// one parity need 8 distinct positions. V: a transposed read touches rows {0..3, 8..11} + 4g at two
-// adjacent chunks; rows of one parity then need positions that differ above bit 0.
-__device__ __forceinline__ int swz8_k(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz8_v(int r) { return 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1); }
+// Chunk swizzles (16-byte chunks; 64 banks x 4 bytes = 16 chunk slots). 128-byte rows alternate
+// between the two halves of the banks by parity, 64-byte rows cycle through four quarters.
+// K: a b128 phase reads chunk c of 16 consecutive rows, so rows that share a bank slot (one parity
+// at d = 128, one residue mod 4 at d = 64) need distinct positions. V: a transposed read touches
+// rows {0..3, 8..11} + 4g at two adjacent chunks per 32 lanes; rows sharing a slot then need
+// positions that differ above bit 0.
+template <int HD>
+__device__ __forceinline__ int swz8_k(int r) {
+  if constexpr (HD == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+template <int HD>
+__device__ __forceinline__ int swz8_v(int r) {
+  if constexpr (HD == 128) return 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1);
+  else return 2 * ((r >> 3) & 1);
+}
 
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // operand formats 0 (E4M3) and unit block scales (E8M0 code 127 = 2^0)
@@ -75,18 +85,23 @@ __device__ __forceinline__ float pair_max8(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <bool CAUSAL>
+template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int H, int group, int N, int n_qtiles, float scale_log2,
-    float v_descale) {
-  __shared__ Fp8Smem sm;
-  constexpr int HD = F8_HD;
+    float v_descale, int split_pairs) {
+  __shared__ Fp8Smem<HD> sm;
+  constexpr int KK = HD / 64;          // 64-deep MFMAs per 32x32 score block
   constexpr int CBLK = HD / 32;        // 32-wide head-dimension blocks of O^T
-  constexpr int RPI = 1024 / HD;       // rows per direct-load wave instruction (8)
-  constexpr int BLOCKS = F8_BC / RPI;  // wave instructions per tensor per tile (8)
+  constexpr int CHUNKS = HD / 16;      // 16-byte chunks per row
+  constexpr int RPI = 1024 / HD;       // rows per direct-load wave instruction (8 or 16)
+  constexpr int BLOCKS = F8_BC / RPI;  // wave instructions per tensor per tile (8 or 4)
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  // With split_pairs the grid holds each causal pair twice: workgroups L and L + half run its heavy
+  // and its light tile (only_rep 0 and 1); otherwise one workgroup runs both (only_rep -1).
+  const int half = split_pairs ? (int)gridDim.x / 2 : (int)gridDim.x;
+  const int item = xcd_remap(blockIdx.x % half, half);
+  const int only_rep = split_pairs ? (int)(blockIdx.x / half) : -1;
   const int per_head = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
   const int pair = item % per_head;
   const int bh = item / per_head;
@@ -106,39 +121,39 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
   const size_t lse_base = ((size_t)b * H + h) * N;
 
   // Causal workgroups take the query tiles (n - 1 - p, p) so every workgroup does the same work.
-  for (int rep = 0; rep < (CAUSAL ? 2 : 1); ++rep) {
+  for (int rep = (only_rep == 1 ? 1 : 0); rep < (CAUSAL && only_rep != 0 ? 2 : 1); ++rep) {
     const int qt = CAUSAL && rep == 0 ? n_qtiles - 1 - pair : pair;
     if (rep == 1 && qt == n_qtiles - 1 - pair) break;
-    if (rep == 1) __syncthreads();  // every wave is done with the first tile's LDS stages
+    if (rep == 1 && only_rep < 0) __syncthreads();  // every wave is done with the first tile's LDS stages
     const int q0 = qt * F8_BR + w * 32;
     const int qi = q0 + l32;
 
     // A negative factor flips the sign bit of every Q code (exact); c > 0 afterwards.
     const bool neg = scale_log2 < 0.f;
     const float c = fmaxf(neg ? -scale_log2 : scale_log2, FLT_MIN);
-    i32x8 qf[2];
+    i32x8 qf[KK];
     if (qi < N) {
       const uint4* src = reinterpret_cast<const uint4*>(Q + q_base + (size_t)qi * HD);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
         qf[kk] = cat16(src[4 * kk + 2 * g], src[4 * kk + 2 * g + 1]);
         if (neg) qf[kk] ^= (int)0x80808080u;
       }
     } else {
-      qf[0] = i32x8{};
-      qf[1] = i32x8{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = i32x8{};
     }
 
     const int q_end = min(N, qt * F8_BR + F8_BR);
     const int n_kt = CAUSAL ? (q_end + F8_BC - 1) / F8_BC : (N + F8_BC - 1) / F8_BC;
 
-    // Direct-to-LDS staging: wave w issues blocks w and w + 4 of a tile (8 rows each); lane i fills
-    // row 8 * blk + i / 8 at chunk position i % 8 with the global chunk position ^ swz(row). Rows
-    // past the sequence end fall outside the buffer resource and load as zeros.
+    // Direct-to-LDS staging: wave w issues blocks w, w + 4, ... of a tile (RPI rows each); lane i
+    // fills row RPI * blk + i / CHUNKS at chunk position i % CHUNKS with the global chunk position
+    // ^ swz(row). Rows past the sequence end fall outside the buffer resource and load as zeros.
     const int BLK_BYTES = 4 * RPI * HD;
-    const int st_row = w * RPI + (lane >> 3);
-    const int k_voff = st_row * HD + (((lane & 7) ^ swz8_k(st_row)) * 16);
-    const int v_voff = st_row * HD + (((lane & 7) ^ swz8_v(st_row)) * 16);
+    const int st_row = w * RPI + lane / CHUNKS;
+    const int k_voff = st_row * HD + (((lane % CHUNKS) ^ swz8_k<HD>(st_row)) * 16);
+    const int v_voff = st_row * HD + (((lane % CHUNKS) ^ swz8_v<HD>(st_row)) * 16);
     const uint8_t* k_head = K + kv_base;
     const uint8_t* v_head = V + kv_base;
     auto tile_bytes = [&](int row0) { return min(N - row0, F8_BC) * HD; };
@@ -159,14 +174,14 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
 
     // K A-operand (S^T block kb, d block kk): row 32kb + l32, chunks 4kk + 2g and 4kk + 2g + 1.
     const int k_lane = l32 * HD;
-    const int k_t = swz8_k(l32);
+    const int k_t = swz8_k<HD>(l32);
     // V^T A-operand: source lane 2k + bsel of a 16-lane group points at key row 16j + v_row and
     // byte column 32cb + 16 * ((lane / 16) % 2) + 8 * bsel; the key rows' swizzle is a lane constant.
     const int v_k = (lane & 15) >> 1;
     const int v_row = 8 * (v_k >> 2) + 4 * g + (v_k & 3);
     const int v_lane = v_row * HD + 8 * (lane & 1);
     const int v_c = (lane >> 4) & 1;
-    const int v_t = swz8_v(v_row);
+    const int v_t = swz8_v<HD>(v_row);
 
     // S^T for one tile: block kb rows = keys 32kb + 8(r/4) + 4g + r%4, column = this lane's query.
     auto scores = [&](const uint8_t* kbuf, f32x16 (&s)[2]) {
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       for (int kb = 0; kb < 2; ++kb) {
         const uint8_t* krow = kbuf + 32 * kb * HD + k_lane;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
           const uint4 a0 = *reinterpret_cast<const uint4*>(krow + (((4 * kk + 2 * g) ^ k_t) * 16));
           const uint4 a1 = *reinterpret_cast<const uint4*>(krow + (((4 * kk + 2 * g + 1) ^ k_t) * 16));
           s[kb] = mfma_f8(cat16(a0, a1), qf[kk], kk == 0 ? f32x16{} : s[kb]);
@@ -327,27 +342,42 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
   }
 }
 
-template <bool CAUSAL>
+template <int HD, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
                   float scale_log2, float v_descale, hipStream_t stream, const char* name) {
   const int n_qt = (N + F8_BR - 1) / F8_BR;
-  const long long total = (long long)(CAUSAL ? (n_qt + 1) / 2 : n_qt) * H * B;
+  long long total = (long long)(CAUSAL ? (n_qt + 1) / 2 : n_qt) * H * B;
+  // A causal grid of pairs that fills fewer than two workgroups per CU runs each pair as two
+  // workgroups, as the bf16 forward does.
+  static int cus = 0;  // CUs of the device (one device per process here), queried once
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess)
+      cus = 0;
+  }
+  const int split = CAUSAL && cus > 0 && total < 2LL * cus ? 1 : 0;
+  if (split) total *= 2;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   TimedScope ts(name, stream);
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3((unsigned)total), dim3(F8_THREADS), 0, stream,
+  hipLaunchKernelGGL((fwd_fp8_kernel<HD, CAUSAL>), dim3((unsigned)total), dim3(F8_THREADS), 0, stream,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v),
-                     static_cast<bf16*>(o), lse, H, H / H_kv, N, n_qt, scale_log2, v_descale);
+                     static_cast<bf16*>(o), lse, H, H / H_kv, N, n_qt, scale_log2, v_descale, split);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
-                          int N, bool causal, float scale, float q_descale, float k_descale, float v_descale,
+                          int N, int d, bool causal, float scale, float q_descale, float k_descale, float v_descale,
                           hipStream_t stream) {
   const float scale_log2 = (float)((double)scale * (double)q_descale * (double)k_descale * 1.4426950408889634);
-  return causal ? launch<true>(q, k, v, o, lse, B, H, H_kv, N, scale_log2, v_descale, stream, "fwd_fp8_d128_causal")
-                : launch<false>(q, k, v, o, lse, B, H, H_kv, N, scale_log2, v_descale, stream, "fwd_fp8_d128");
+  if (d == 128)
+    return causal ? launch<128, true>(q, k, v, o, lse, B, H, H_kv, N, scale_log2, v_descale, stream,
+                                      "fwd_fp8_d128_causal")
+                  : launch<128, false>(q, k, v, o, lse, B, H, H_kv, N, scale_log2, v_descale, stream, "fwd_fp8_d128");
+  return causal ? launch<64, true>(q, k, v, o, lse, B, H, H_kv, N, scale_log2, v_descale, stream, "fwd_fp8_d64_causal")
+                : launch<64, false>(q, k, v, o, lse, B, H, H_kv, N, scale_log2, v_descale, stream, "fwd_fp8_d64");
 }
 
 }  // namespace ra

@@ -33,10 +33,10 @@ hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, v
                                   const int32_t* cu_seqlens, int B, int max_seqlen, int T, int H, int H_kv, int d,
                                   bool causal, float scale, hipStream_t stream);
 
-// fp8 (E4M3) inputs, d = 128: q [B,H,N,128], k, v [B,H_kv,N,128] uint8 codes; o bf16; real inputs are
-// descale * decoded code.
+// fp8 (E4M3) inputs, d = 64 or 128: q [B,H,N,d], k, v [B,H_kv,N,d] uint8 codes; o bf16; real inputs
+// are descale * decoded code.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
-                          int N, bool causal, float scale, float q_descale, float k_descale, float v_descale,
+                          int N, int d, bool causal, float scale, float q_descale, float k_descale, float v_descale,
                           hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

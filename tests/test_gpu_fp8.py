@@ -128,12 +128,14 @@ def full_check(lib, t, causal, scale, descale, label):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("B,H,H_kv,N", [(1, 2, 2, 333), (2, 8, 2, 200), (1, 2, 2, 1), (1, 1, 1, 129),
-                                         (1, 2, 2, 600), (2, 4, 4, 64), (1, 4, 1, 127)])
-def test_fp8_shapes(lib, B, H, H_kv, N, causal):
-    w = I.Workload("fp8_case", "fwd", B, H, H_kv, N, 128, "e4m3", causal, seed=21)
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 333, 128), (2, 8, 2, 200, 128), (1, 2, 2, 1, 128),
+                                           (1, 1, 1, 129, 128), (1, 2, 2, 600, 128), (2, 4, 4, 64, 128),
+                                           (1, 4, 1, 127, 128), (1, 2, 2, 333, 64), (2, 4, 2, 200, 64),
+                                           (1, 1, 1, 1, 64), (1, 2, 1, 600, 64)])
+def test_fp8_shapes(lib, B, H, H_kv, N, d, causal):
+    w = I.Workload("fp8_case", "fwd", B, H, H_kv, N, d, "e4m3", causal, seed=21)
     t = I.make_fp8_prefill(w)
-    full_check(lib, t, causal, w.scale, t["descale"], f"fp8 B{B} H{H}/{H_kv} N{N} causal={causal}")
+    full_check(lib, t, causal, w.scale, t["descale"], f"fp8 B{B} H{H}/{H_kv} N{N} d{d} causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -144,10 +146,11 @@ def test_fp8_arbitrary_descales_and_negative_scale(lib, causal):
     full_check(lib, t, causal, -0.07, ds, f"fp8 descales {ds} scale -0.07")
 
 
-def test_fp8_zero_scale_is_the_mean(lib):
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_zero_scale_is_the_mean(lib, d):
     """scale 0: every probability is 2^6 exactly, so O is the mean of V up to the matrix unit's
     truncation (t * sum_j |v_j| / count) and the bf16 output rounding; LSE = ln(count)."""
-    w = I.Workload("fp8_zero", "fwd", 1, 2, 2, 300, 128, "e4m3", True, seed=23)
+    w = I.Workload("fp8_zero", "fwd", 1, 2, 2, 300, d, "e4m3", True, seed=23)
     t = I.make_fp8_prefill(w)
     o, lse = run(lib, t, True, 0.0)
     v = real(t["v"], t["descale"][2])
