@@ -212,3 +212,19 @@ def test_fp8_prefill_4k_sampled_rows_and_a_head(lib, name):
     flat = np.concatenate([np.stack([np.full(len(ii), b), np.full(len(ii), h), ii], 1) for b, h, ii in rows_by_head])
     ro, rl = orc.attention_fwd_fp8_rows(t["q"].numpy(), t["k"].numpy(), t["v"].numpy(), ds, w.causal, w.scale, flat)
     check(o, lse, q, k, v, w.causal, w.scale, rows_by_head, ro, rl, name)
+
+
+def test_fp8_prefill_16k_sampled_rows(lib):
+    """A long fp8 sequence (128 query tiles): sampled rows within the derived bound."""
+    w = I.Workload("fp8_16k", "fwd", 1, 2, 2, 16384, 128, "e4m3", False, seed=28, qk_factor=0.5)
+    t = I.make_fp8_prefill(w)
+    o, lse = run(lib, t, w.causal, w.scale)
+    ds = t["descale"]
+    q, k, v = (real(t[n], s) for n, s in zip("qkv", ds))
+    groups = {}
+    for b, h, i in sample_rows(w.B, w.H, w.N, 100, seed=28):
+        groups.setdefault((int(b), int(h)), set()).add(int(i))
+    rows_by_head = [(b, h, np.array(sorted(ii))) for (b, h), ii in sorted(groups.items())]
+    flat = np.concatenate([np.stack([np.full(len(ii), b), np.full(len(ii), h), ii], 1) for b, h, ii in rows_by_head])
+    ro, rl = orc.attention_fwd_fp8_rows(t["q"].numpy(), t["k"].numpy(), t["v"].numpy(), ds, w.causal, w.scale, flat)
+    check(o, lse, q, k, v, w.causal, w.scale, rows_by_head, ro, rl, "fp8_16k")

@@ -108,6 +108,20 @@ def test_prefill_4k_sampled_rows_and_heads(lib, name):
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_16k_sampled_rows(lib, causal):
+    """A long sequence (128 query tiles, 64 causal pairs per head): sampled rows against the oracle."""
+    w = I.Workload("prefill_16k", "fwd", 1, 2, 2, 16384, 128, "bf16", causal, seed=16, qk_factor=0.5)
+    t, o, lse = run_fwd(lib, w)
+    rows = sample_rows(w.B, w.H, w.N, 120, seed=16)
+    ro, rl = orc.attention_fwd_rows(f64(t["q"]), f64(t["k"]), f64(t["v"]), causal, w.scale, rows)
+    og = f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lg = f64(lse)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    e, el = float(np.max(np.abs(og - ro))), float(np.max(np.abs(lg - rl)))
+    print(f"prefill_16k causal={causal}: max|dO|={e:.3e} max|dLSE|={el:.3e}")
+    assert e <= TOL_BF16 and el <= TOL_BF16
+
+
 def test_causal_row0_and_constant_v(lib):
     w = I.Workload("inv", "fwd", 1, 2, 2, 300, 128, "bf16", True, seed=13)
     t = I.make_prefill(w, with_dout=False)
