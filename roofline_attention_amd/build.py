@@ -38,6 +38,23 @@ def _compile(src: str, extra=(), objdir=OBJ) -> str:
     return out
 
 
+CEILINGS_SRC = "ceilings.hip"
+CEILINGS_EXE = os.path.join(PKG, "ceilings")
+
+
+def build_ceilings(verbose: bool = False) -> str:
+    """Compiles the ceiling microbenchmarks (csrc/ceilings.hip) into the `ceilings` executable."""
+    tmp = CEILINGS_EXE + ".tmp"
+    cmd = [hipcc(), *HIPFLAGS, os.path.join(CSRC, CEILINGS_SRC), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEILINGS_SRC}:\n{r.stderr}")
+    os.replace(tmp, CEILINGS_EXE)
+    if verbose:
+        print(f"built {CEILINGS_EXE}")
+    return CEILINGS_EXE
+
+
 def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB) -> str:
     """Compiles every source and links the library; extra_flags/lib_path build a tuning variant."""
     objdir = OBJ if lib_path == LIB else lib_path + ".objs"
@@ -57,4 +74,5 @@ def build(verbose: bool = False, extra_flags=(), lib_path: str = LIB) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_ceilings(verbose=True)
     sys.exit(0)
