@@ -18,8 +18,9 @@
 //   * The V^T operand of O^T = V^T P^T comes from ds_read_b64_tr_b16, which transposes 16-bit
 //     elements across each 16-lane group, so V is never transposed in memory.
 //   * Software pipeline: while the softmax of tile j runs on the vector ALUs, the score MFMAs of
-//     tile j+1 are issued from the same basic block, so one wave keeps the matrix cores fed. K is
-//     therefore loaded one tile ahead of V (two LDS stages each, one barrier per tile).
+//     tile j+1 are issued beside it, so one wave keeps the matrix cores fed (a vector instruction
+//     overlaps an MFMA on gfx950 only when both come from the same wave). K is therefore loaded
+//     one tile ahead of V (two LDS stages each, one barrier per tile).
 //   * The running maximum is only raised when a tile's maximum exceeds it by more than 8 (log2
 //     units); the numerator and the normaliser always share the same reference, so the result is
 //     unchanged while the output rescale is skipped on almost every tile.
@@ -225,6 +226,15 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       }
     };
 
+    // One 32-key half (block kb) of S^T for one tile.
+    auto scores_half = [&](const bf16* kbuf, f32x16 (&s)[2], int kb) {
+      s[kb] = f32x16{};
+      const bf16* krow = &kbuf[32 * kb * HD + k_lane];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ k_t) * 8), qf[kk], s[kb]);
+    };
+
     f32x16 oacc[CBLK];
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x16{};
@@ -243,10 +253,10 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       }
     };
 
-    // Online-softmax step on raw scores s: updates the reference maximum and the normaliser and
-    // returns P^T in the B-operand layout (k-step ks = 2kb + hh takes accumulator slots 8hh..8hh+7).
-    // The output rescale, needed only when the maximum rises, is left to the caller.
-    auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4], float& alpha) {
+    // Online-softmax step on raw scores s, in two parts around the (rare) output rescale.
+    // decide: the tile maximum, the reference maximum and the rescale factor alpha; returns whether
+    // any lane of the wave raised its reference (the caller then rescales the output accumulator).
+    auto decide = [&](f32x16 (&s)[2], float& alpha) {
       // Row maximum over the 32 scores as a tree of 3-input maxima. fmaximum (NaN-propagating)
       // equals fmaxf on the finite or -inf scores here and needs no NaN-quieting of its inputs.
       float m1[11];
@@ -265,10 +275,15 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       const float m_new = raise ? tmax : m_run;
       alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
+      return __builtin_amdgcn_ballot_w64(raise) != 0;
+    };
+    // probs: P^T = 2^(s c - m) in the B-operand layout (k-step ks = 2kb + hh takes accumulator
+    // slots 8hh..8hh+7) and the normaliser update.
+    auto probs = [&](const f32x16 (&s)[2], bf16x8 (&pf)[4], float alpha) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pf[2 * kb + (r >> 3)][r & 7] = to_bf16(fast_exp2(fmaf(s[kb][r], c, -m_new)));
+        for (int r = 0; r < 16; ++r) pf[2 * kb + (r >> 3)][r & 7] = to_bf16(fast_exp2(fmaf(s[kb][r], c, -m_run)));
       }
       // The normaliser sums the same bf16-rounded probabilities that multiply V, two per
       // instruction (bf16 dot product with (1, 1), fp32 accumulation).
@@ -279,9 +294,6 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
         for (int e = 0; e < 8; e += 2) tsum = bf16_pair_sum(pf[i][e], pf[i][e + 1], tsum);
       }
       l_run = fmaf(l_run, alpha, tsum);
-      // The branch condition reads tsum so the exponentials stay ahead of the (rare) rescale branch,
-      // in the basic block that also issues the next tile's score MFMAs.
-      return __builtin_amdgcn_ballot_w64(raise && tsum >= 0.f) != 0;
     };
 
     // O^T += V^T P^T. A operand: lane row c = 32cb + l32, keys 32kb + 16hh + {4g..4g+3, 8+4g..8+4g+3}.
@@ -324,12 +336,17 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
       bf16x8 pf[4];
       float alpha;
-      scores(sm.k[(kt + 1) & 1], sn);                // matrix cores: tile kt + 1
-      const bool rescale = softmax(sc, pf, alpha);  // vector ALUs: tile kt
-      if (rescale) {
+      // The rescale branch ends a basic block, and the compiler interleaves vector work only with
+      // MFMAs of the same block: the first half of tile kt + 1's score MFMAs goes with the maximum
+      // before the branch, the second half with the exponentials after it, where O += V P of tile
+      // kt (which needs them) follows in the same block.
+      scores_half(sm.k[(kt + 1) & 1], sn, 0);  // matrix cores: tile kt + 1, keys 0..31
+      if (decide(sc, alpha)) {                 // vector ALUs: tile kt
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
       }
+      scores_half(sm.k[(kt + 1) & 1], sn, 1);  // keys 32..63
+      probs(sc, pf, alpha);
       pv(sm.v[kt & 1], pf);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of V_{kt+1}, K_{kt+2} have landed
       __syncthreads();                // ... and every wave's; stages read in this step are free
@@ -339,10 +356,11 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
       bf16x8 pf[4];
       float alpha;
-      if (softmax(sc, pf, alpha)) {
+      if (decide(sc, alpha)) {
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
       }
+      probs(sc, pf, alpha);
       pv(sm.v[kt & 1], pf);
     };
     // Two steps per trip so the two score buffers trade roles instead of being copied.
