@@ -183,18 +183,20 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
     const int v_c = (lane >> 4) & 1;
     const int v_t = swz8_v<HD>(v_row);
 
-    // S^T for one tile: block kb rows = keys 32kb + 8(r/4) + 4g + r%4, column = this lane's query.
-    auto scores = [&](const uint8_t* kbuf, f32x16 (&s)[2]) {
+    // S^T for one tile, one 32-key block kb at a time: rows = keys 32kb + 8(r/4) + 4g + r%4,
+    // column = this lane's query.
+    auto scores_half = [&](const uint8_t* kbuf, f32x16 (&s)[2], int kb) {
+      const uint8_t* krow = kbuf + 32 * kb * HD + k_lane;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint8_t* krow = kbuf + 32 * kb * HD + k_lane;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const uint4 a0 = *reinterpret_cast<const uint4*>(krow + (((4 * kk + 2 * g) ^ k_t) * 16));
-          const uint4 a1 = *reinterpret_cast<const uint4*>(krow + (((4 * kk + 2 * g + 1) ^ k_t) * 16));
-          s[kb] = mfma_f8(cat16(a0, a1), qf[kk], kk == 0 ? f32x16{} : s[kb]);
-        }
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 a0 = *reinterpret_cast<const uint4*>(krow + (((4 * kk + 2 * g) ^ k_t) * 16));
+        const uint4 a1 = *reinterpret_cast<const uint4*>(krow + (((4 * kk + 2 * g + 1) ^ k_t) * 16));
+        s[kb] = mfma_f8(cat16(a0, a1), qf[kk], kk == 0 ? f32x16{} : s[kb]);
       }
+    };
+    auto scores = [&](const uint8_t* kbuf, f32x16 (&s)[2]) {
+      scores_half(kbuf, s, 0);
+      scores_half(kbuf, s, 1);
     };
 
     f32x16 oacc[CBLK];
@@ -214,9 +216,10 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       }
     };
 
-    // Online-softmax step on raw scores: updates the reference maximum and the normaliser and
-    // returns P^T as E4M3 codes in the B-operand byte order (byte 16kb + r <- accumulator s[kb][r]).
-    auto softmax = [&](f32x16 (&s)[2], i32x8& pf, float& alpha) {
+    // Online-softmax step on raw scores, in two parts around the (rare) output rescale. decide:
+    // the tile maximum, the reference maximum and alpha; returns whether any lane of the wave raised
+    // its reference (the caller then rescales the output accumulator).
+    auto decide = [&](f32x16 (&s)[2], float& alpha) {
       float m1[11];
 #pragma unroll
       for (int i = 0; i < 10; ++i) {
@@ -232,7 +235,12 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       const float m_new = raise ? tmax : m_run;
       alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
-      const float bias = kPOffset - m_new;
+      return __builtin_amdgcn_ballot_w64(raise) != 0;
+    };
+    // probs: P^T as E4M3 codes in the B-operand byte order (byte 16kb + r <- accumulator s[kb][r])
+    // and the normaliser update.
+    auto probs = [&](const f32x16 (&s)[2], i32x8& pf, float alpha) {
+      const float bias = kPOffset - m_run;
       float p[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -250,7 +258,6 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       }
       const float tsum = ((t8[0] + t8[1]) + (t8[2] + t8[3])) + ((t8[4] + t8[5]) + (t8[6] + t8[7]));
       l_run = fmaf(l_run, alpha, tsum);
-      return __builtin_amdgcn_ballot_w64(raise && tsum >= 0.f) != 0;
     };
 
     // O^T += V^T P^T: one 64-key MFMA per 32 output columns.
@@ -291,12 +298,15 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       if (is_boundary(kt)) apply_mask(kt * F8_BC, sc);
       i32x8 pf;
       float alpha;
-      scores(sm.k[(kt + 1) & 1], sn);
-      const bool rescale = softmax(sc, pf, alpha);
-      if (rescale) {
+      // As in the bf16 forward: the maximum goes with the first half of tile kt+1's score MFMAs
+      // before the rescale branch, the exponentials with the second half and O += V P after it.
+      scores_half(sm.k[(kt + 1) & 1], sn, 0);
+      if (decide(sc, alpha)) {
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
       }
+      scores_half(sm.k[(kt + 1) & 1], sn, 1);
+      probs(sc, pf, alpha);
       pv(sm.v[kt & 1], pf);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -305,10 +315,11 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       if (is_boundary(kt)) apply_mask(kt * F8_BC, sc);
       i32x8 pf;
       float alpha;
-      if (softmax(sc, pf, alpha)) {
+      if (decide(sc, alpha)) {
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
       }
+      probs(sc, pf, alpha);
       pv(sm.v[kt & 1], pf);
     };
     f32x16 s_alt[2];
