@@ -147,6 +147,48 @@ def test_one_hot_selection(lib):
     assert float((o.cpu().float()[0, 0] - v.float()[0, 0, sel]).abs().max()) <= TOL_BF16
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jump_beyond_exp_range(lib, d, causal):
+    # Every row's maximum sits in a late key tile and exceeds all earlier scores by 200 (scale 1):
+    # 2^(200 log2 e) overflows fp32, so the reference maximum must be raised from the raw scores
+    # of that tile, not from exponentials taken against the earlier one. Row i selects key
+    # N/2 + i mod (N/2) (non-causal) or key i itself (causal, rows >= N/2).
+    N = 256
+    half = N // 2
+    k = torch.zeros(1, 1, N, d)
+    k[0, 0, half + torch.arange(half), torch.arange(half) % d] = 1.0
+    q = torch.zeros(1, 1, N, d)
+    q[0, 0, torch.arange(N), torch.arange(N) % d] = 200.0
+    v = torch.from_numpy(I.normal_block(15, 2, 0, 0, (N, d))).view(1, 1, N, d)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    o, lse = lib.fwd(dev(q), dev(k), dev(v), causal, 1.0)
+    ro, rl = orc.attention_fwd(f64(q), f64(k), f64(v), causal, 1.0)
+    assert np.isfinite(o.cpu().float().numpy()).all()
+    assert max_err(o, ro) <= TOL_BF16
+    assert float(np.max(np.abs(lse.cpu().numpy() - rl))) <= TOL_BF16
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_below_and_above_the_lazy_threshold(lib, causal):
+    # Scores (log2 units) are 0 on keys 0..63, 7 on keys 64..255 (every probability near 2^7 against
+    # the first reference, which stays: no raise) and 14 on keys 256..511 (a raise).
+    N, d = 512, 128
+    beta = torch.zeros(N)
+    beta[64:256] = 7.0 * math.log(2.0)
+    beta[256:] = 14.0 * math.log(2.0)
+    k = torch.zeros(1, 1, N, d)
+    k[0, 0, :, 0] = beta
+    q = torch.zeros(1, 1, N, d)
+    q[0, 0, :, 0] = 1.0
+    v = torch.from_numpy(I.normal_block(16, 2, 0, 0, (N, d))).view(1, 1, N, d)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    o, lse = lib.fwd(dev(q), dev(k), dev(v), causal, 1.0)
+    ro, rl = orc.attention_fwd(f64(q), f64(k), f64(v), causal, 1.0)
+    assert max_err(o, ro) <= TOL_BF16
+    assert float(np.max(np.abs(lse.cpu().numpy() - rl))) <= TOL_BF16
+
+
 def test_forward_is_deterministic(lib):
     w = I.Workload("det", "fwd", 2, 4, 4, 520, 128, "bf16", True, seed=15)
     t = I.make_prefill(w, with_dout=False)
