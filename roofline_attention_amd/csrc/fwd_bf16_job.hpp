@@ -23,7 +23,11 @@
 //     one tile ahead of V (two LDS stages each, one barrier per tile).
 //   * The running maximum is only raised when a tile's maximum exceeds it by more than 8 (log2
 //     units); the numerator and the normaliser always share the same reference, so the result is
-//     unchanged while the output rescale is skipped on almost every tile.
+//     unchanged while the output rescale is skipped on almost every tile. The probabilities are
+//     first taken against the current reference; only when some lane's bf16 row sum reaches 2^8
+//     (so a probability might exceed 2^8, or the reference is still unset) does the tile take the
+//     exact path: row maximum, raise decision, rescale, probabilities again. Below 2^8 no raise is
+//     possible, so the result is that of deciding on every tile, without the maximum on most.
 //   * Masks are applied only on tiles that cross the causal diagonal or the sequence end.
 //   * Workgroup ids are remapped so the query tiles of one head run on one XCD (shared L2); a causal
 //     workgroup runs a heavy and a light query tile so every workgroup carries the same work.
@@ -253,10 +257,10 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       }
     };
 
-    // Online-softmax step on raw scores s, in two parts around the (rare) output rescale.
-    // decide: the tile maximum, the reference maximum and the rescale factor alpha; returns whether
-    // any lane of the wave raised its reference (the caller then rescales the output accumulator).
-    auto decide = [&](f32x16 (&s)[2], float& alpha) {
+    // Exact lazy-raise decision for raw scores s: the tile maximum, the new reference maximum and
+    // the rescale factor alpha; returns whether any lane of the wave raised its reference (the
+    // caller then rescales the output accumulator).
+    auto decide = [&](const f32x16 (&s)[2], float& alpha) {
       // Row maximum over the 32 scores as a tree of 3-input maxima. fmaximum (NaN-propagating)
       // equals fmaxf on the finite or -inf scores here and needs no NaN-quieting of its inputs.
       float m1[11];
@@ -277,23 +281,40 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       m_run = m_new;
       return __builtin_amdgcn_ballot_w64(raise) != 0;
     };
-    // probs: P^T = 2^(s c - m) in the B-operand layout (k-step ks = 2kb + hh takes accumulator
-    // slots 8hh..8hh+7) and the normaliser update.
-    auto probs = [&](const f32x16 (&s)[2], bf16x8 (&pf)[4], float alpha) {
+    // P^T = 2^(s c - m_run) in the B-operand layout (k-step ks = 2kb + hh takes accumulator slots
+    // 8hh..8hh+7); returns this lane's sum of the bf16-rounded probabilities, which are what
+    // multiplies V (bf16 dot products with (1, 1), fp32 accumulation).
+    auto probs = [&](const f32x16 (&s)[2], bf16x8 (&pf)[4]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pf[2 * kb + (r >> 3)][r & 7] = to_bf16(fast_exp2(fmaf(s[kb][r], c, -m_run)));
       }
-      // The normaliser sums the same bf16-rounded probabilities that multiply V, two per
-      // instruction (bf16 dot product with (1, 1), fp32 accumulation).
       float tsum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) tsum = bf16_pair_sum(pf[i][e], pf[i][e + 1], tsum);
       }
-      l_run = fmaf(l_run, alpha, tsum);
+      return tsum;
+    };
+    // Online-softmax step on raw scores s: P^T of the tile and the normaliser update, the output
+    // rescaled when the reference rises. Against the current reference every probability of a
+    // lane is at most its row sum, so a sum below 2^8 rules out a raise (any score more than 8 above
+    // the reference gives a probability that rounds to at least 2^8); otherwise (or on an infinite
+    // or NaN sum: reference unset) the exact decision runs and the probabilities are taken again.
+    auto softmax = [&](const f32x16 (&s)[2], bf16x8 (&pf)[4]) {
+      float tsum = probs(s, pf);
+      if (__builtin_amdgcn_ballot_w64(!(tsum < 256.f)) != 0) {
+        float alpha;
+        if (decide(s, alpha)) {
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+        }
+        l_run *= alpha;
+        tsum = probs(s, pf);
+      }
+      l_run += tsum;
     };
 
     // O^T += V^T P^T. A operand: lane row c = 32cb + l32, keys 32kb + 16hh + {4g..4g+3, 8+4g..8+4g+3}.
@@ -335,18 +356,12 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       if (kt + 2 < n_kt) issue_k(kt + 2, kt & 1);
       if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
       bf16x8 pf[4];
-      float alpha;
-      // The rescale branch ends a basic block, and the compiler interleaves vector work only with
-      // MFMAs of the same block: the first half of tile kt + 1's score MFMAs goes with the maximum
-      // before the branch, the second half with the exponentials after it, where O += V P of tile
-      // kt (which needs them) follows in the same block.
+      // The (rare) exact path of the softmax is a branch, and the compiler interleaves vector work
+      // only with MFMAs of the same basic block: the first half of tile kt + 1's score MFMAs goes
+      // with the exponentials before the branch, the second half with O += V P of tile kt after it.
       scores_half(sm.k[(kt + 1) & 1], sn, 0);  // matrix cores: tile kt + 1, keys 0..31
-      if (decide(sc, alpha)) {                 // vector ALUs: tile kt
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
-      }
+      softmax(sc, pf);                          // vector ALUs: tile kt
       scores_half(sm.k[(kt + 1) & 1], sn, 1);  // keys 32..63
-      probs(sc, pf, alpha);
       pv(sm.v[kt & 1], pf);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of V_{kt+1}, K_{kt+2} have landed
       __syncthreads();                // ... and every wave's; stages read in this step are free
@@ -355,12 +370,12 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
     auto last = [&](int kt, f32x16 (&sc)[2]) {
       if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
       bf16x8 pf[4];
-      float alpha;
+      float alpha;  // the exact path directly: one tile, nothing to overlap
       if (decide(sc, alpha)) {
 #pragma unroll
         for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
       }
-      probs(sc, pf, alpha);
+      l_run = fmaf(l_run, alpha, probs(sc, pf));
       pv(sm.v[kt & 1], pf);
     };
     // Two steps per trip so the two score buffers trade roles instead of being copied.
