@@ -17,6 +17,7 @@
 // Output: one JSON line on stdout. Every kernel stays inside its own buffers and LDS arrays.
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cstdio>
 #include <cstdlib>
 
@@ -34,6 +35,19 @@ typedef float f2 __attribute__((ext_vector_type(2)));
       exit(1);                                                                    \
     }                                                                             \
   } while (0)
+
+// Calls launch() until 0.2 s of wall time have passed, synchronising every 8 launches.
+template <class F>
+void warm_up(F launch) {
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int n = 1;; ++n) {
+    launch();
+    if (n % 8 == 0) {
+      CHECK(hipDeviceSynchronize());
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(200)) break;
+    }
+  }
+}
 
 // ----------------------------------------------------------------------------------- MFMA ----
 
@@ -72,12 +86,14 @@ void mfma_rate(int cus, double& tflops, double& cycles_per_inst) {
   unsigned long long* cyc;
   CHECK(hipMalloc(&out, (size_t)grid * 256 * 4));
   CHECK(hipMalloc(&cyc, (size_t)grid * 8));
-  hipLaunchKernelGGL(mfma_kernel<KIND>, dim3(grid), dim3(256), 0, 0, out, cyc, 3);  // warm-up
+  // Untimed launches for 0.2 s first: the clock takes tens of milliseconds of load to ramp up.
+  warm_up([&] { hipLaunchKernelGGL(mfma_kernel<KIND>, dim3(grid), dim3(256), 0, 0, out, cyc, 3); });
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
+  constexpr int kTimed = 10;
   CHECK(hipEventRecord(e0));
-  hipLaunchKernelGGL(mfma_kernel<KIND>, dim3(grid), dim3(256), 0, 0, out, cyc, 3);
+  for (int i = 0; i < kTimed; ++i) hipLaunchKernelGGL(mfma_kernel<KIND>, dim3(grid), dim3(256), 0, 0, out, cyc, 3);
   CHECK(hipEventRecord(e1));
   CHECK(hipEventSynchronize(e1));
   float ms = 0.f;
@@ -85,7 +101,7 @@ void mfma_rate(int cus, double& tflops, double& cycles_per_inst) {
   unsigned long long c0 = 0;
   CHECK(hipMemcpy(&c0, cyc, 8, hipMemcpyDeviceToHost));
   const double flops_per_inst = KIND == 0 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
-  const double insts = (double)grid * 4 /* waves */ * MFMA_IT * 4;
+  const double insts = (double)kTimed * grid * 4 /* waves */ * MFMA_IT * 4;
   tflops = insts * flops_per_inst / (ms * 1e-3) / 1e12;
   // one wave per SIMD issuing independent MFMAs: cycles between its instructions = pipe occupancy
   cycles_per_inst = (double)c0 / (MFMA_IT * 4);
@@ -122,7 +138,8 @@ void hbm(int cus, double& read_gbs, double& copy_gbs) {
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
   float best_r = 1e30f, best_c = 1e30f;
-  for (int rep = 0; rep < 4; ++rep) {
+  warm_up([&] { hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, 0, a, n, out); });
+  for (int rep = 0; rep < 6; ++rep) {
     float ms = 0.f;
     CHECK(hipEventRecord(e0));
     hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, 0, a, n, out);
