@@ -123,7 +123,9 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
  *   `causal` is accepted for signature symmetry and ignored: the single query follows every key.
  *   workspace: device buffer of at least attn_decode_workspace_size(B, H, N_cap, d) bytes,
  *   16-byte aligned, contents need no initialisation; it is scratch owned by the caller.
- * dtype must be ATTN_BF16; H / H_kv must be 1, 2, 4 or 8; B * H_kv must be below 2^24.
+ * dtype must be ATTN_BF16. Any group size g = H / H_kv: g = 1, 2, 4, 8 have kernels of their own;
+ * other g run a 16-column kernel over chunks of up to 16 query heads (for g > 16 each chunk reads
+ * the KV head's rows again). B * H_kv * (g in {1,2,4,8} ? 1 : ceil(g / 16)) must be below 2^24.
  */
 size_t attn_decode_workspace_size(int B, int H, int N_cap, int d);
 attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -144,7 +146,7 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
  *   is then unspecified).
  *   page_size: a power of two in [32, 1024] (a 32-key tile then never straddles a page).
  *   workspace: at least attn_decode_workspace_size(B, H, max_pages * page_size, d) bytes.
- * dtype must be ATTN_BF16; H / H_kv in {1, 2, 4, 8}; B * H_kv < 2^24.
+ * dtype must be ATTN_BF16; group sizes and the grid limit as for attn_decode.
  */
 attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
                               const int32_t* kv_len, const int32_t* block_table, int B, int H, int H_kv,

@@ -238,9 +238,9 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports ATTN_BF16 only");
   const int G = H / H_kv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ATTN_ERR_UNSUPPORTED, "decode group size H/H_kv must be 1, 2, 4 or 8");
-  if ((long long)B * H_kv >= (1LL << 24))
-    return fail(ATTN_ERR_INVALID_ARG, "decode needs B * H_kv < 2^24 (one grid row of workgroups)");
+  const long long chunks = (G == 1 || G == 2 || G == 4 || G == 8) ? 1 : (G + 15) / 16;
+  if ((long long)B * H_kv * chunks >= (1LL << 24))
+    return fail(ATTN_ERR_INVALID_ARG, "decode needs B * H_kv * ceil(G / 16) < 2^24 (one grid row of workgroups)");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(kv_len) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
@@ -278,9 +278,9 @@ attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "decode supports ATTN_BF16 only");
   const int G = H / H_kv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(ATTN_ERR_UNSUPPORTED, "decode group size H/H_kv must be 1, 2, 4 or 8");
-  if ((long long)B * H_kv >= (1LL << 24))
-    return fail(ATTN_ERR_INVALID_ARG, "decode needs B * H_kv < 2^24 (one grid row of workgroups)");
+  const long long chunks = (G == 1 || G == 2 || G == 4 || G == 8) ? 1 : (G + 15) / 16;
+  if ((long long)B * H_kv * chunks >= (1LL << 24))
+    return fail(ATTN_ERR_INVALID_ARG, "decode needs B * H_kv * ceil(G / 16) < 2^24 (one grid row of workgroups)");
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
     return fail(ATTN_ERR_INVALID_ARG, "q, pages and o must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(kv_len) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||

@@ -82,36 +82,47 @@ struct DecodeMerge {
 // hold a multiple of 32 rows), so each tile is one contiguous run read through its own buffer
 // resource. Page ids are looked up two tiles ahead of their loads and clamped into
 // [0, num_pages), so a malformed table cannot send a load outside the caches.
+// G = 1, 2, 4 or 8: the group size, exactly. G = kDecodeAnyGroup: any group size `grp` (= H / H_kv),
+// taken in chunks of up to 16 query heads, one workgroup per chunk (for grp > 16 each chunk reads
+// the KV head's rows again).
+constexpr int kDecodeAnyGroup = 16;
+
 template <int HD, int G, bool PAGED>
 __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
     const bf16* __restrict__ Qd, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int32_t* __restrict__ kv_len, float* __restrict__ ws, int H, int H_kv, int N_cap,
     int n_split, float scale_log2, const int32_t* __restrict__ block_table, int max_pages, int page_shift,
-    int num_pages) {
+    int num_pages, int grp, int n_chunk) {
   constexpr int CH = HD / 8;        // 16-byte chunks per row
   constexpr int KSTEPS = HD / 32;   // 16x16x32 k-steps over d
   constexpr int CB = HD / 16;       // 16-row blocks of O^T
   constexpr int VROWS = 64 / CH;    // V rows per wave load instruction
   constexpr int VLOADS = DEC_TILE / VROWS;
   constexpr int REC = HD + 4;
-  static_assert(G <= 16, "query heads per KV head");
+  static_assert(G <= 16, "query heads per workgroup");
   __shared__ bf16 vtile[DEC_WAVES][DEC_TILE * HD];
   __shared__ DecodeMerge<HD, G> mg;
 
-  // Grid (B * H_kv, n_split), x fastest: workgroups reach the 8 XCDs round-robin in launch order,
-  // so consecutive ids walk the (sequence, KV head) pairs of one split and every XCD gets an even
-  // share of each split. (With the split index fastest, split s would always land on XCD s mod 8
-  // and short sequences would load only the first few XCDs.)
+  // Grid (B * H_kv * n_chunk, n_split), x fastest: workgroups reach the 8 XCDs round-robin in
+  // launch order, so consecutive ids walk the (sequence, KV head, head chunk) triples of one split
+  // and every XCD gets an even share of each split. (With the split index fastest, split s would
+  // always land on XCD s mod 8 and short sequences would load only the first few XCDs.)
+  constexpr bool ANY = G == kDecodeAnyGroup;
   const int split = blockIdx.y;
-  const int hk = blockIdx.x % H_kv;
-  const int b = blockIdx.x / H_kv;
+  const int chunk = ANY ? (int)blockIdx.x % n_chunk : 0;
+  const int bk = ANY ? (int)blockIdx.x / n_chunk : (int)blockIdx.x;
+  const int hk = bk % H_kv;
+  const int b = bk / H_kv;
+  const int gsize = ANY ? grp : G;                                // query heads per KV head
+  const int head0 = hk * gsize + 16 * chunk;                      // first query head of this workgroup
+  const int gh = ANY ? min(16, gsize - 16 * chunk) : G;           // query heads of this workgroup
   const int len = clamp_len(kv_len, b, N_cap);
   const int k_begin = split * kDecodeSplit;
   if (k_begin >= len) return;  // uniform over the workgroup, before any barrier
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int col = lane & 15;  // MFMA column = query head of the group (valid when < G)
+  const int col = lane & 15;  // MFMA column = query head head0 + col (valid when < gh)
   const int q4 = lane >> 4;   // 16-lane group
   const int kw_begin = k_begin + w * DEC_WAVE_KEYS;
   const int kw_end = min(len, kw_begin + DEC_WAVE_KEYS);
@@ -119,12 +130,12 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
   const int n_tiles = (n_keys + DEC_TILE - 1) / DEC_TILE;
   bf16* vt = vtile[w];
 
-  // Q^T as the B operand: column col = head hk*G + col, k-group q4 holds d = 32kk + 8q4 .. +7.
+  // Q^T as the B operand: column col = head head0 + col, k-group q4 holds d = 32kk + 8q4 .. +7.
   bf16x8 qf[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    qf[kk] = col < G ? *reinterpret_cast<const bf16x8*>(Qd + ((size_t)b * H + hk * G + col) * HD + 32 * kk + 8 * q4)
-                     : bf16x8{};
+    qf[kk] = col < gh ? *reinterpret_cast<const bf16x8*>(Qd + ((size_t)b * H + head0 + col) * HD + 32 * kk + 8 * q4)
+                      : bf16x8{};
   }
 
   const size_t head = PAGED ? 0 : ((size_t)b * H_kv + hk) * (size_t)N_cap * HD;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
 
-  if (col < G) {
+  if (col < gh) {
     if (q4 == 0) {
       mg.m[w][col] = m_run;  // -inf for a wave with no keys
       mg.l[w][col] = l_run;
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
   }
   __syncthreads();
   constexpr int PER = HD / 64;
-  for (int hq = w; hq < G; hq += DEC_WAVES) {
+  for (int hq = w; hq < gh; hq += DEC_WAVES) {
     float M = mg.m[0][hq];  // wave 0 always has keys
 #pragma unroll
     for (int v = 1; v < DEC_WAVES; ++v) M = fmaxf(M, mg.m[v][hq]);
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
 #pragma unroll
       for (int e = 0; e < PER; ++e) o[e] = fmaf(wgt, mg.o[v][hq][lane * PER + e], o[e]);
     }
-    float* rec = ws + (((size_t)b * H + hk * G + hq) * n_split + split) * REC;
+    float* rec = ws + (((size_t)b * H + head0 + hq) * n_split + split) * REC;
     if (lane == 0) {
       rec[0] = M;
       rec[1] = L;
@@ -383,12 +394,14 @@ hipError_t launch(const void* q, const void* kc, const void* vc, void* o, float*
                   const char* split_name, const char* combine_name, const int32_t* block_table, int max_pages,
                   int page_shift, int num_pages) {
   const int n_split = (N_cap + kDecodeSplit - 1) / kDecodeSplit;
+  const int grp = H / H_kv;
+  const int n_chunk = G == kDecodeAnyGroup ? (grp + 15) / 16 : 1;
   {
     TimedScope ts(split_name, stream);
-    hipLaunchKernelGGL((decode_split_kernel<HD, G, PAGED>), dim3(B * H_kv, n_split), dim3(DEC_WAVES * 64), 0, stream,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(kc), static_cast<const bf16*>(vc),
-                       kv_len, static_cast<float*>(ws), H, H_kv, N_cap, n_split, scale * kLog2e, block_table,
-                       max_pages, page_shift, num_pages);
+    hipLaunchKernelGGL((decode_split_kernel<HD, G, PAGED>), dim3(B * H_kv * n_chunk, n_split), dim3(DEC_WAVES * 64),
+                       0, stream, static_cast<const bf16*>(q), static_cast<const bf16*>(kc),
+                       static_cast<const bf16*>(vc), kv_len, static_cast<float*>(ws), H, H_kv, N_cap, n_split,
+                       scale * kLog2e, block_table, max_pages, page_shift, num_pages, grp, n_chunk);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -424,7 +437,10 @@ hipError_t launch_g(int G, const void* q, const void* kc, const void* vc, void* 
     case 8: return launch<HD, 8, PAGED>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
                                         PAGED ? "decode_paged_split_g8" : "decode_split_g8", comb, pg.table,
                                         pg.max_pages, pg.page_shift, pg.num_pages);
-    default: return hipErrorInvalidValue;
+    default:
+      return launch<HD, kDecodeAnyGroup, PAGED>(q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream,
+                                                PAGED ? "decode_paged_split_any" : "decode_split_any", comb,
+                                                pg.table, pg.max_pages, pg.page_shift, pg.num_pages);
   }
 }
 

@@ -145,7 +145,7 @@ def test_decode_validation(lib):
     assert call(ws_bytes=ws_need - 1) == WORKSPACE
     assert call(ws=None) == WORKSPACE
     assert call(dtype=F32) == UNSUPPORTED
-    assert call(H=48, H_kv=4) == UNSUPPORTED  # group of 12
+    assert call(B=65535, H=4352, H_kv=256) == INVALID  # groups of 17: two 16-head chunks, beyond one grid row
     assert call(H=30) == INVALID
     assert call(kv=None) == INVALID
     assert call(d=80) == UNSUPPORTED
@@ -168,7 +168,6 @@ def test_decode_paged_validation(lib):
     assert call(P=0) == INVALID
     assert call(max_pages=0) == INVALID
     assert call(ws_bytes=ws_need - 4) == WORKSPACE
-    assert call(H=48, H_kv=4) == UNSUPPORTED
     assert call(dtype=F32) == UNSUPPORTED
     assert call(table=ctypes.c_void_p(BASE + 6 * GAP + 2)) == INVALID
 

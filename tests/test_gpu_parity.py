@@ -292,7 +292,10 @@ def test_decode_gqa_full_workload(lib):
     assert eo <= TOL_BF16 and el <= TOL_BF16
 
 
-@pytest.mark.parametrize("H,H_kv,d", [(8, 8, 128), (8, 4, 64), (16, 4, 128), (16, 2, 128), (8, 1, 64)])
+# Group sizes 1, 2, 4, 8 have kernels of their own; 3, 7, 16 run the 16-column kernel in one
+# chunk, 40 in three (16 + 16 + 8 query heads).
+@pytest.mark.parametrize("H,H_kv,d", [(8, 8, 128), (8, 4, 64), (16, 4, 128), (16, 2, 128), (8, 1, 64),
+                                      (12, 4, 128), (14, 2, 64), (16, 1, 128), (40, 1, 128)])
 def test_decode_ragged_lengths(lib, H, H_kv, d):
     w = I.Workload("dec", "decode", 7, H, H_kv, 1100, d, "bf16", False, seed=16, kv_lo=1, kv_hi=1100)
     eo, el = decode_check(lib, w, kv_len=[1, 255, 257, 1023, 1024, 1025, 1100])
@@ -307,7 +310,7 @@ def test_decode_more_than_64_splits(lib):
 
 
 @pytest.mark.parametrize("page_size", [32, 64, 256])
-@pytest.mark.parametrize("H,H_kv,d", [(8, 8, 128), (8, 4, 64), (16, 2, 128)])
+@pytest.mark.parametrize("H,H_kv,d", [(8, 8, 128), (8, 4, 64), (16, 2, 128), (10, 2, 128), (32, 1, 64)])
 def test_decode_paged_matches_dense_and_oracle(lib, H, H_kv, d, page_size):
     # Same rows as the contiguous cache, scattered over shuffled pages: the result must equal the
     # contiguous decode bit for bit (same arithmetic, other addresses) and the paged oracle.
