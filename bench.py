@@ -188,14 +188,12 @@ def main():
 
     # Algorithmic work per launch of each kernel of the step. The backward's five products are
     # assigned where they are first computed: S, dP, dV, dK in the key-major kernel, dQ in the
-    # query-major kernel; the preprocess is HBM-bound (reads O and dO, writes D).
+    # query-major kernel (which also computes the rows' D from O and dO).
     Nsq = w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
     work = {
         "fwd_bf16_d128_causal": ("mfma", 4.0 * Nsq),
         "bwd_dkdv_d128_causal": ("mfma", 8.0 * Nsq),
         "bwd_dq_d128_causal": ("mfma", 2.0 * Nsq),
-        # reads O, dO and LSE; writes D and LSE * log2 e
-        "bwd_pre_d128": ("hbm", 2.0 * 2 * w.B * w.H * w.N * w.d + 12.0 * w.B * w.H * w.N),
     }
     kernels = {}
     for name, st in stats.items():

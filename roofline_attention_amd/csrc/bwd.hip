@@ -9,15 +9,15 @@
 // is recomputing S and dP in both the key-major and the query-major kernel; persisting dS instead
 // doubled DRAM traffic in the same paper (section 4.7).
 //
-// Kernels, per (batch, head):
-//   bwd_pre : D_i = sum_t dO[i,t] * O[i,t]   (equals sum_j P_ij dP_ij), and LSE_i * log2 e
+// Kernels, per (batch, head), in this order:
+//   bwd_dq  : workgroup = 128 queries (4 waves x 32, Q and dO of its rows in registers); first the
+//             rows' D_i = sum_t dO[i,t] O[i,t] (equals sum_j P_ij dP_ij) and LSE_i log2 e, written
+//             out for the key-major kernel; then it streams 64-key tiles of K and V: S^T = K Q^T,
+//             P^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T; stores dQ * scale.
 //   bwd_dkdv: workgroup = 128 keys (4 waves x 32, K and V of its keys in registers); streams
 //             64-query tiles of Q, dO, LSE and D through three LDS stages:
 //             S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e), dV += P^T dO, dP = dO V^T,
 //             dS = P (dP - D), dK += dS^T Q; stores dK * scale and dV.
-//   bwd_dq  : workgroup = 128 queries (4 waves x 32, Q and dO of its rows in registers); streams
-//             64-key tiles of K and V: S^T = K Q^T, P^T, dP^T = V dO^T, dS^T = P^T (dP^T - D),
-//             dQ^T += K^T dS^T; stores dQ * scale.
 // MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to bf16 (nearest
 // even) as MFMA operands. The probabilities and dS come out of the score accumulators already in
 // the A/B-operand layout their next product needs. Operands that contract over the rows of a
@@ -31,35 +31,6 @@
 namespace ra {
 namespace {
 
-// ------------------------------------------------------------------------- preprocess ----
-
-template <int HD>
-__global__ __launch_bounds__(BWD_THREADS) void bwd_pre_kernel(const bf16* __restrict__ O,
-                                                              const bf16* __restrict__ dO,
-                                                              const float* __restrict__ LSE,
-                                                              float* __restrict__ D, float* __restrict__ L2,
-                                                              long long rows) {
-  constexpr int CH = HD / 8;
-  constexpr int RPB = BWD_THREADS / CH;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CH;
-  const int c = threadIdx.x % CH;
-  float x = 0.f;
-  if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(O + row * HD + c * 8);
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + row * HD + c * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x = fmaf(to_f32(a[e]), to_f32(g[e]), x);
-  }
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));
-  if constexpr (CH == 16)
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true));
-  if (row < rows && c == 0) {
-    D[row] = x;
-    L2[row] = LSE[row] * kLog2e;  // the row's LSE in log2 units, streamed by the key-major kernel
-  }
-}
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -74,18 +45,18 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dQ, int H, int group, int N, int n_qtiles, float scale, float scale_log2) {
+    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dg,
+    float* __restrict__ L2, float* __restrict__ dQ, int H, int group, int N, int n_qtiles, float scale,
+    float scale_log2) {
   __shared__ DqSmem<HD> sm;
-  bwd_dq_job<HD, CAUSAL>(Q, K, V, dO, LSE, Dg, dQ, H, group, N, n_qtiles, scale, scale_log2, sm,
-                         xcd_remap(blockIdx.x, gridDim.x));
+  bwd_dq_job<HD, CAUSAL, true>(Q, K, V, dO, LSE, Dg, dQ, H, group, N, n_qtiles, scale, scale_log2, sm,
+                               xcd_remap(blockIdx.x, gridDim.x), O, L2);
 }
 
 template <int HD, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int H_kv, int N,
-                  float scale, void* ws, hipStream_t stream, const char* pre_name, const char* dkdv_name,
-                  const char* dq_name) {
+                  float scale, void* ws, hipStream_t stream, const char* dkdv_name, const char* dq_name) {
   const bf16* Q = static_cast<const bf16*>(q);
   const bf16* K = static_cast<const bf16*>(k);
   const bf16* V = static_cast<const bf16*>(v);
@@ -94,19 +65,19 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   const long long rows = (long long)B * H * N;
   float* D = static_cast<float*>(ws);  // workspace: D [B,H,N], then LSE * log2 e [B,H,N]
   float* L2 = D + rows;
-  constexpr int RPB = BWD_THREADS / (HD / 8);
-  {
-    TimedScope ts(pre_name, stream);
-    hipLaunchKernelGGL((bwd_pre_kernel<HD>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(BWD_THREADS), 0,
-                       stream, O, dO, lse, D, L2, rows);
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   const int n_t = (N + 127) / 128;
   const int n_wg = CAUSAL ? (n_t + 1) / 2 : n_t;  // causal workgroups take a pair of tiles
   const int n_wg_kv = CAUSAL && RA_DKDV_PAIR ? (n_t + 1) / 2 : n_t;
   const unsigned total = (unsigned)((long long)n_wg * H * B);           // dQ: per query head
   const unsigned total_kv = (unsigned)((long long)n_wg_kv * H_kv * B);  // dK, dV: per KV head
+  // dQ first: it also writes every row's D and LSE * log2 e, which the key-major kernel streams.
+  {
+    TimedScope ts(dq_name, stream);
+    hipLaunchKernelGGL((bwd_dq_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, stream, Q, K, V, O, dO, lse,
+                       D, L2, dq, H, H / H_kv, N, n_t, scale, scale * kLog2e);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   const size_t dkdv_smem = sizeof(DkdvSmem<HD>);
   static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
   if (!attr_set) {
@@ -119,13 +90,6 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
     TimedScope ts(dkdv_name, stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total_kv), dim3(BWD_THREADS), dkdv_smem, stream, Q, K,
                        V, dO, L2, D, dk, dv, H, H / H_kv, N, n_t, scale, scale * kLog2e);
-  }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  {
-    TimedScope ts(dq_name, stream);
-    hipLaunchKernelGGL((bwd_dq_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, stream, Q, K, V, dO, lse,
-                       D, dq, H, H / H_kv, N, n_t, scale, scale * kLog2e);
   }
   return hipGetLastError();
 }
@@ -142,14 +106,14 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       bool causal, float scale, void* ws, hipStream_t stream) {
   if (d == 128) {
     return causal ? launch<128, true>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
-                                      "bwd_pre_d128", "bwd_dkdv_d128_causal", "bwd_dq_d128_causal")
+                                      "bwd_dkdv_d128_causal", "bwd_dq_d128_causal")
                   : launch<128, false>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
-                                       "bwd_pre_d128", "bwd_dkdv_d128", "bwd_dq_d128");
+                                       "bwd_dkdv_d128", "bwd_dq_d128");
   }
   return causal ? launch<64, true>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
-                                   "bwd_pre_d64", "bwd_dkdv_d64_causal", "bwd_dq_d64_causal")
+                                   "bwd_dkdv_d64_causal", "bwd_dq_d64_causal")
                 : launch<64, false>(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, scale, ws, stream,
-                                    "bwd_pre_d64", "bwd_dkdv_d64", "bwd_dq_d64");
+                                    "bwd_dkdv_d64", "bwd_dq_d64");
 }
 
 }  // namespace ra

@@ -295,12 +295,15 @@ struct DqSmem {
 
 // One work item of the query-major kernel: the query tile(s) of `item` (a pair under a causal
 // mask), with the workgroup's LDS stages `sm`.
-template <int HD, bool CAUSAL>
+// ROW_TERMS: the job also computes its rows' D_i = sum_c dO[i,c] O[i,c] from O (bf16) and dO, and
+// writes D and LSE * log2 e (what the key-major job streams) to Dg and L2; otherwise it reads D
+// from Dg.
+template <int HD, bool CAUSAL, bool ROW_TERMS = false>
 __device__ __forceinline__ void bwd_dq_job(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dg,
     float* __restrict__ dQ, int H, int group, int N, int n_qtiles, float scale, float scale_log2,
-    DqSmem<HD>& sm, int item) {
+    DqSmem<HD>& sm, int item, const bf16* __restrict__ O = nullptr, float* __restrict__ L2 = nullptr) {
   constexpr int KSTEPS = HD / 16;
   constexpr int CBLK = HD / 32;
 
@@ -337,10 +340,28 @@ __device__ __forceinline__ void bwd_dq_job(
         df[kk] = ds[2 * kk + g];
       }
       lse2 = LSE[rowbase + qi] * kLog2e;
-      Dq = Dg[rowbase + qi];
+      if constexpr (ROW_TERMS) {
+        // This lane's half of the row (chunks 2kk + g, as qf and df).
+        const bf16x8* os = reinterpret_cast<const bf16x8*>(O + head + (size_t)qi * HD);
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const bf16x8 a = os[2 * kk + g];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) Dq = fmaf(to_f32(a[e]), to_f32(df[kk][e]), Dq);
+        }
+      } else {
+        Dq = Dg[rowbase + qi];
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = df[kk] = bf16x8{};
+    }
+    if constexpr (ROW_TERMS) {
+      Dq += __shfl_xor(Dq, 32, 64);  // the other half of the row (lane l32 + 32)
+      if (qi < N && g == 0) {
+        Dg[rowbase + qi] = Dq;
+        L2[rowbase + qi] = lse2;  // the row's LSE in log2 units, streamed by the key-major job
+      }
     }
 
     f32x16 acc[CBLK];
