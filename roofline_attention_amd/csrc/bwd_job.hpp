@@ -220,7 +220,7 @@ __device__ __forceinline__ void bwd_dkdv_job(
       const size_t qrows = (size_t)b * H + (size_t)hk * group + j;
       Qh = Q + qrows * N * HD;
       dOh = dO + qrows * N * HD;
-      LSEh = LSE2 + qrows * N;  // LSE * log2 e, from the preprocess
+      LSEh = LSE2 + qrows * N;  // LSE * log2 e, written by the dQ kernel (or the fused forward)
       Dh = Dg + qrows * N;
       // Every wave has finished reading the previous head's tiles before this head's prologue
       // writes LDS.

@@ -17,7 +17,7 @@
 //
 // Each item is the same device code as the separate kernels (fwd_bf16_job, bwd_dq_job,
 // bwd_dkdv_job), so results match them; D here is summed from the rounded O in a different
-// order than the separate preprocess, a float32 rounding-level difference. The one launch takes
+// order than in the separate dQ kernel, a float32 rounding-level difference. The one launch takes
 // the largest register and LDS footprint of its phases (the key-major item: about 400 registers and
 // 97.5 KB of LDS), so every phase runs at one workgroup of 4 waves per CU.
 #include <hip/hip_cooperative_groups.h>
