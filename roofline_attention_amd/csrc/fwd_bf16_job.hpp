@@ -368,6 +368,9 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
     };
     // The last tile: softmax and O += V P only.
     auto last = [&](int kt, f32x16 (&sc)[2]) {
+      // Under a causal mask the last key tile can lie wholly above this wave's rows (the first
+      // waves of a workgroup on its second diagonal tile): every probability is 0, nothing to add.
+      if (CAUSAL && kt * FWD_BC > q0 + 31) return;
       if (is_boundary(kt)) apply_mask(kt * FWD_BC, sc);
       bf16x8 pf[4];
       float alpha;  // the exact path directly: one tile, nothing to overlap
