@@ -306,3 +306,43 @@ def attention_bwd(q, k, v, dout, causal: bool, scale: float):
             dq[b, h] = scale * (ds @ k[b, hk])
             dk[b, hk] += scale * (ds.T @ q[b, h])
     return dq, dk, dv, o, lse
+
+
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens, causal: bool, scale: float):
+    """Gradients of L = sum(O * dO) for the ragged prefill of attention_fwd_varlen.
+
+    q, dout [T, H, d], k/v [T, H_kv, d], cu_seqlens as in attention_fwd_varlen. Returns
+    (dq [T, H, d], dk [T, H_kv, d], dv [T, H_kv, d], o [T, H, d], lse [H, T]). Sequences share
+    no score, so each sequence's gradients are the steps of attention_bwd taken on its own rows
+    r0 .. r1 - 1 of every head, with causal positions counted from r0.
+    """
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    T, H, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (T, H_kv, d) or v.shape != k.shape or dout.shape != q.shape or H % H_kv != 0:
+        raise ValueError("expected q, dout [T,H,d], k/v [T,H_kv,d] with H % H_kv == 0")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, end at T and not decrease")
+    g = H // H_kv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    o = np.zeros_like(q)
+    lse = np.zeros((H, T))
+    for b in range(len(cu) - 1):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        if r1 == r0:
+            continue
+        for h in range(H):
+            hk = h // g
+            qs, ks, vs, dos = q[r0:r1, h], k[r0:r1, hk], v[r0:r1, hk], dout[r0:r1, h]
+            p, lse[h, r0:r1] = _softmax_rows(_scores(qs, ks, causal, scale))
+            os_ = p @ vs
+            o[r0:r1, h] = os_
+            dv[r0:r1, hk] += p.T @ dos
+            dp = dos @ vs.T
+            ds = p * (dp - np.sum(dos * os_, axis=1, keepdims=True))
+            dq[r0:r1, h] = scale * (ds @ ks)
+            dk[r0:r1, hk] += scale * (ds.T @ qs)
+    return dq, dk, dv, o, lse

@@ -36,6 +36,10 @@ MUTANTS = {
     "varlen_crosses_sequences": ("s = _scores(q[r0:r1, h], k[r0:r1, hk], causal, scale)",
                                  "s = _scores(q[r0:r1, h], k[:r1, hk], causal, scale)"),
     "varlen_rows_global_causal": ("k_end = t + 1 if causal else r1", "k_end = t + 1 - r0 if causal else r1"),
+    "varlen_bwd_dk_overwrites_group": ("dk[r0:r1, hk] += scale * (ds.T @ qs)", "dk[r0:r1, hk] = scale * (ds.T @ qs)"),
+    "varlen_bwd_drops_D": ("ds = p * (dp - np.sum(dos * os_, axis=1, keepdims=True))", "ds = p * dp"),
+    "varlen_bwd_gqa_modulo_map": ("            hk = h // g\n            qs, ks", "            hk = h % H_kv\n            qs, ks"),
+    "varlen_bwd_dv_not_transposed": ("dv[r0:r1, hk] += p.T @ dos", "dv[r0:r1, hk] += p @ dos"),
     "paged_wrong_page": ("pages = table[b, :(n + ps - 1) // ps]", "pages = table[b, 1:(n + ps - 1) // ps + 1]"),
     "paged_reads_first_head": ("np.asarray(k_pages[p, hk], dtype=np.float64) for p in pages",
                                "np.asarray(k_pages[p, 0], dtype=np.float64) for p in pages"),
@@ -72,6 +76,8 @@ PIN_CALLS = [
     (pins.test_bwd_causal_last_key, {}),
     (pins.test_varlen_equals_block_diagonal_mask, dict(causal=True, H=4, H_kv=2)),
     (pins.test_varlen_rows_agree_with_full, dict(causal=True)),
+    (pins.test_varlen_bwd_matches_autograd_with_block_diagonal_mask, dict(causal=True, H=4, H_kv=2)),
+    (pins.test_varlen_bwd_finite_differences, {}),
     (pins.test_decode_paged_equals_contiguous, dict(shuffle=True)),
     (pins.test_decode_paged_matches_sdpa, {}),
     (pins.test_e4m3_decode_matches_torch_on_every_code, {}),
