@@ -174,6 +174,24 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Ragged backward: attn_bwd over the packed rows of attn_fwd_varlen. Sequences share no score, so
+ * each sequence's gradients are those attn_bwd computes for one (batch) entry of its length, with
+ * causal positions counted from its first row; the same two atomic-free kernels run over the
+ * packed rows, each workgroup covering one sequence's rows.
+ *   q, o, dout [T, H, d] bf16; k, v [T, H_kv, d] bf16; lse [H, T] float32 from attn_fwd_varlen on
+ *   the same q, k, v, cu_seqlens, causal and scale. dq [T, H, d], dk, dv [T, H_kv, d] float32:
+ *   every row of every sequence is overwritten. cu_seqlens, max_seqlen, T and the clamping of
+ *   malformed offsets as for attn_fwd_varlen; T == 0 returns ATTN_OK without device work.
+ *   workspace: at least attn_bwd_varlen_workspace_size(T, H, d) bytes, 16-byte aligned, scratch.
+ * dtype must be ATTN_BF16; d in {64, 128}; H % H_kv == 0.
+ */
+size_t attn_bwd_varlen_workspace_size(int T, int H, int d);
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, float* dq, float* dk, float* dv, const int32_t* cu_seqlens,
+                            int B, int max_seqlen, int T, int H, int H_kv, int d, int causal, float scale,
+                            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward and backward in ONE launch, with no atomic accumulation: the fused forward+backward of
  * the MoA paper ("Validating Memory-Optimal Transformer Kernels on Real Hardware", sections
  * 4.4-4.5), whose GPU version lost to the unfused pair while dK and dV were accumulated with atomics

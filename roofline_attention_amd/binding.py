@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("ROOFATTN_LIB", os.path.join(_HERE, "libroofattn.so"))
 
 ATTN_F32, ATTN_BF16 = 0, 1
 # The ABI version these signatures describe (attn_abi_version() of the matching library).
-ABI_VERSION = 5
+ABI_VERSION = 6
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 # Every symbol include/attn.h declares, with (restype, argtypes).
@@ -40,6 +40,9 @@ SIGNATURES = {
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
+    "attn_bwd_varlen_workspace_size": (_Z, [_I, _I, _I]),
+    "attn_bwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z,
+                             _P]),
     "attn_fwd_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_fwd_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_timing_enable": (_I, [_I]),
@@ -289,6 +292,49 @@ def bwd(q, k, v, o, dout, lse, causal: bool, scale: Optional[float] = None, dq=N
     _check(_lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                          B, H, H_kv, N, d, int(bool(causal)), float(scale), ATTN_BF16, _ptr(workspace),
                          workspace.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
+def bwd_varlen_workspace_size(T: int, H: int, d: int) -> int:
+    return int(_lib.attn_bwd_varlen_workspace_size(T, H, d))
+
+
+def bwd_varlen(q, k, v, o, dout, lse, cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool,
+               scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None):
+    """Ragged backward: bf16 q, o, dout [T,H,d], k, v [T,H_kv,d], fp32 lse [H,T] from fwd_varlen and
+    cu_seqlens [B+1] int32 on the GPU.
+
+    Returns fp32 (dq [T,H,d], dk, dv [T,H_kv,d])."""
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [T, H, d]")
+    T, H, d = q.shape
+    H_kv = k.shape[1]
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, (T, H_kv, d), q.device)
+    for name, t in (("o", o), ("dout", dout)):
+        _need(t, name, torch.bfloat16, q.shape, q.device)
+    _need(lse, "lse", torch.float32, (H, T), q.device)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, None, q.device)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with B + 1 >= 2 entries")
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(k.shape, **f32) if dk is None else dk
+    dv = torch.empty(v.shape, **f32) if dv is None else dv
+    _need(dq, "dq", torch.float32, q.shape, q.device)
+    _need(dk, "dk", torch.float32, k.shape, q.device)
+    _need(dv, "dv", torch.float32, v.shape, q.device)
+    need = bwd_varlen_workspace_size(T, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, None, q.device)
+    _check(_lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(cu_seqlens), B, int(max_seqlen), T, H, H_kv, d, int(bool(causal)),
+                                float(scale), ATTN_BF16, _ptr(workspace), workspace.numel(), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -131,7 +131,7 @@ TimedScope::~TimedScope() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 5; }
+int attn_abi_version(void) { return 6; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -338,6 +338,47 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
       if (overlap(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
   return hip_status(ra::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, causal != 0, scale, workspace,
                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_varlen_workspace_size(int T, int H, int d) {
+  if (T < 0 || H < 1 || (d != 64 && d != 128)) return 0;
+  return ra::bwd_varlen_workspace_bytes(T, H, d);
+}
+
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, float* dq, float* dk, float* dv, const int32_t* cu_seqlens, int B,
+                            int max_seqlen, int T, int H, int H_kv, int d, int causal, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !cu_seqlens)
+    return fail(ATTN_ERR_INVALID_ARG, "all tensor pointers and cu_seqlens must be non-null");
+  if (T < 0) return fail(ATTN_ERR_INVALID_ARG, "T must be >= 0");
+  attn_status st = check_shape(B, H, H_kv, max_seqlen, d, scale);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "ragged backward supports ATTN_BF16 only");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(ATTN_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, "lse and cu_seqlens must be 4-byte aligned");
+  const size_t need = ra::bwd_varlen_workspace_bytes(T, H, d);
+  if (T > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "ragged backward workspace too small");
+  if (workspace && !aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const long long tiles = (long long)((max_seqlen + 127) / 128) * H * B;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_ERR_INVALID_ARG, "problem too large for one launch");
+  const size_t tb = (size_t)T * H * d * 2, kb = (size_t)T * H_kv * d * 2, gb = (size_t)T * H * d * 4,
+               gkb = (size_t)T * H_kv * d * 4, lb = (size_t)H * T * 4;
+  const Range ins[] = {{q, tb}, {k, kb}, {v, kb}, {o, tb}, {dout, tb}, {lse, lb}, {cu_seqlens, (size_t)(B + 1) * 4}};
+  const Range outs[] = {{dq, gb}, {dk, gkb}, {dv, gkb}, {workspace, T > 0 ? need : 0}};
+  for (const Range& a : outs)
+    for (const Range& b : ins)
+      if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
+  if (T == 0) return ok();  // no rows
+  return hip_status(ra::launch_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_seqlen, T, H, H_kv,
+                                          d, causal != 0, scale, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_fwd_bwd_workspace_size(int B, int H, int N, int d) {

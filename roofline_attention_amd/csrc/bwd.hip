@@ -53,6 +53,33 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
                                xcd_remap(blockIdx.x, gridDim.x), O, L2);
 }
 
+// Ragged batches: the same jobs over packed token rows. The (sequence, head) groups of work items
+// are dealt round-robin over the XCDs, as in the ragged forward, so that every XCD gets an equal
+// share of every sequence.
+template <int HD, bool CAUSAL>
+__global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_varlen_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dg,
+    float* __restrict__ dK, float* __restrict__ dV, const int32_t* __restrict__ cu_seqlens, int T, int H,
+    int group, int N, int n_ktiles, float scale, float scale_log2) {
+  extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+  bwd_dkdv_job<HD, CAUSAL, true>(Q, K, V, dO, LSE2, Dg, dK, dV, H, group, N, n_ktiles, scale, scale_log2,
+                                 *reinterpret_cast<DkdvSmem<HD>*>(dyn_smem),
+                                 xcd_group_remap(blockIdx.x, gridDim.x, n_ktiles), cu_seqlens, T);
+}
+
+template <int HD, bool CAUSAL>
+__global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_varlen_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dg,
+    float* __restrict__ L2, float* __restrict__ dQ, const int32_t* __restrict__ cu_seqlens, int T, int H,
+    int group, int N, int n_qtiles, float scale, float scale_log2) {
+  __shared__ DqSmem<HD> sm;
+  const int per = CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+  bwd_dq_job<HD, CAUSAL, true, true>(Q, K, V, dO, LSE, Dg, dQ, H, group, N, n_qtiles, scale, scale_log2, sm,
+                                     xcd_group_remap(blockIdx.x, gridDim.x, group * per), O, L2, cu_seqlens, T);
+}
+
 template <int HD, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, float* dq, float* dk, float* dv, int B, int H, int H_kv, int N,
@@ -94,7 +121,69 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   return hipGetLastError();
 }
 
+template <int HD, bool CAUSAL>
+hipError_t launch_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, float* dq, float* dk, float* dv, const int32_t* cu_seqlens, int B,
+                         int max_seqlen, int T, int H, int H_kv, float scale, void* ws, hipStream_t stream,
+                         const char* dkdv_name, const char* dq_name) {
+  const bf16* Q = static_cast<const bf16*>(q);
+  const bf16* K = static_cast<const bf16*>(k);
+  const bf16* V = static_cast<const bf16*>(v);
+  const bf16* O = static_cast<const bf16*>(o);
+  const bf16* dO = static_cast<const bf16*>(dout);
+  float* D = static_cast<float*>(ws);  // workspace: D [H,T], then LSE * log2 e [H,T]
+  float* L2 = D + (size_t)H * T;
+  const int n_t = (max_seqlen + 127) / 128;
+  const int n_wg = CAUSAL ? (n_t + 1) / 2 : n_t;
+  const unsigned total = (unsigned)((long long)n_wg * H * B);
+  const unsigned total_kv = (unsigned)((long long)n_t * H_kv * B);
+  {
+    TimedScope ts(dq_name, stream);
+    hipLaunchKernelGGL((bwd_dq_varlen_kernel<HD, CAUSAL>), dim3(total), dim3(BWD_THREADS), 0, stream, Q, K, V, O,
+                       dO, lse, D, L2, dq, cu_seqlens, T, H, H / H_kv, max_seqlen, n_t, scale, scale * kLog2e);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t dkdv_smem = sizeof(DkdvSmem<HD>);
+  static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
+  if (!attr_set) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_varlen_kernel<HD, CAUSAL>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dkdv_smem);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  {
+    TimedScope ts(dkdv_name, stream);
+    hipLaunchKernelGGL((bwd_dkdv_varlen_kernel<HD, CAUSAL>), dim3(total_kv), dim3(BWD_THREADS), dkdv_smem, stream,
+                       Q, K, V, dO, L2, D, dk, dv, cu_seqlens, T, H, H / H_kv, max_seqlen, n_t, scale,
+                       scale * kLog2e);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t bwd_varlen_workspace_bytes(int T, int H, int d) {
+  (void)d;
+  return 2 * (size_t)H * T * sizeof(float);  // D and LSE * log2 e per (head, token) row
+}
+
+hipError_t launch_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, float* dq, float* dk, float* dv, const int32_t* cu_seqlens, int B,
+                             int max_seqlen, int T, int H, int H_kv, int d, bool causal, float scale, void* ws,
+                             hipStream_t stream) {
+  if (d == 128) {
+    return causal ? launch_varlen<128, true>(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_seqlen, T, H, H_kv,
+                                             scale, ws, stream, "bwd_dkdv_varlen_d128_causal",
+                                             "bwd_dq_varlen_d128_causal")
+                  : launch_varlen<128, false>(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_seqlen, T, H,
+                                              H_kv, scale, ws, stream, "bwd_dkdv_varlen_d128", "bwd_dq_varlen_d128");
+  }
+  return causal ? launch_varlen<64, true>(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_seqlen, T, H, H_kv,
+                                          scale, ws, stream, "bwd_dkdv_varlen_d64_causal", "bwd_dq_varlen_d64_causal")
+                : launch_varlen<64, false>(q, k, v, o, dout, lse, dq, dk, dv, cu_seqlens, B, max_seqlen, T, H, H_kv,
+                                           scale, ws, stream, "bwd_dkdv_varlen_d64", "bwd_dq_varlen_d64");
+}
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;

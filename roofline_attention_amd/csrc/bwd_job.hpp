@@ -87,16 +87,22 @@ struct DkdvSmem {
 // workgroup follows any query.
 // One work item of the key-major kernel: the key tile(s) of `item` (ordering below), with the
 // workgroup's LDS stages `sm`.
-template <int HD, bool CAUSAL>
+// Rows: dense [B, H, N, d] queries and [B, H_kv, N, d] keys with N rows per sequence, LSE2 and D
+// [B, H, N]; or, with VARLEN, packed token rows [T, H, d] and [T, H_kv, d] with sequence b at rows
+// cu_seqlens[b] .. cu_seqlens[b+1] - 1 (N the longest length the grid covers), LSE2 and D [H, T].
+// Offsets read from cu_seqlens are clamped into [0, T] and lengths to N, as in the forward.
+template <int HD, bool CAUSAL, bool VARLEN = false>
 __device__ __forceinline__ void bwd_dkdv_job(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, int H, int group, int N, int n_ktiles, float scale,
-    float scale_log2, DkdvSmem<HD>& sm, int item) {
+    float scale_log2, DkdvSmem<HD>& sm, int item, const int32_t* __restrict__ cu_seqlens = nullptr,
+    int T = 0) {
   constexpr int KSTEPS = HD / 16;
   constexpr int CBLK = HD / 32;
 
   constexpr bool PAIR = CAUSAL && RA_DKDV_PAIR;
+  static_assert(!(VARLEN && PAIR), "a ragged batch runs one key tile per workgroup");
   const int per = PAIR ? (n_ktiles + 1) / 2 : n_ktiles;  // workgroups per (sequence, KV head)
   const int pair = item % per;
   const int bhk = item / per;  // (sequence, KV head)
@@ -109,6 +115,15 @@ __device__ __forceinline__ void bwd_dkdv_job(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
+  int Nb = N, start = 0;  // this sequence's rows and (packed) first row
+  if constexpr (VARLEN) {
+    start = min(max(cu_seqlens[b], 0), T);
+    const int end = min(max(cu_seqlens[b + 1], start), T);
+    Nb = min(end - start, N);
+  }
+  const int rs_q = VARLEN ? H * HD : HD;     // element distance between query rows
+  const int rs_kv = VARLEN ? Hkv * HD : HD;  // ... and between key rows
+
   // With RA_DKDV_PAIR a causal workgroup takes the key tiles (p, n - 1 - p) one after the other so
   // every workgroup carries the same work (as the forward and dQ do). For this kernel, at one
   // workgroup per CU, it measured slower at N >= 4096 (4096: 454 vs 417 us, 8192: 853 vs 735 us)
@@ -118,14 +133,16 @@ __device__ __forceinline__ void bwd_dkdv_job(
     if (rep == 1 && kt == pair) break;  // odd tile count: the middle tile runs once
     // every wave is done with the first tile's LDS stages
     if (rep == 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const size_t head = (size_t)bhk * N * HD;  // K, V, dK, dV rows of this KV head
+    if (VARLEN && kt * 128 >= Nb) return;  // key tile past this sequence (uniform over the workgroup)
+    // K, V, dK, dV rows of this KV head
+    const size_t head = VARLEN ? ((size_t)start * Hkv + hk) * HD : (size_t)bhk * N * HD;
     const int kw0 = kt * 128 + w * 32;  // this wave's first key
     const int key = kw0 + l32;          // the key column this lane holds in S and dP
 
     bf16x8 kf[KSTEPS], vf[KSTEPS];
-    if (key < N) {
-      const bf16x8* ks = reinterpret_cast<const bf16x8*>(K + head + (size_t)key * HD);
-      const bf16x8* vs = reinterpret_cast<const bf16x8*>(V + head + (size_t)key * HD);
+    if (key < Nb) {
+      const bf16x8* ks = reinterpret_cast<const bf16x8*>(K + head + (size_t)key * rs_kv);
+      const bf16x8* vs = reinterpret_cast<const bf16x8*>(V + head + (size_t)key * rs_kv);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         kf[kk] = ks[2 * kk + g];
@@ -149,16 +166,24 @@ __device__ __forceinline__ void bwd_dkdv_job(
     const bf16* dOh = nullptr;
     const float* LSEh = nullptr;
     const float* Dh = nullptr;
-    const int n_qt = (N + BWD_BQ - 1) / BWD_BQ;
+    const int n_qt = (Nb + BWD_BQ - 1) / BWD_BQ;
 
     auto stage_of = [](int t) { return (t + DKDV_STAGES) % DKDV_STAGES; };  // t >= -1
     auto stage = [&](int qt) {
       const int s = stage_of(qt);
       const int r0 = qt * BWD_BQ;
-      stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(Qh, r0, N, sm.q[s], w, lane);
-      stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(dOh, r0, N, sm.dO[s], w, lane);
-      if (w == 0) load_to_lds<4>(dma_rsrc(LSEh + r0, (N - r0) * 4), lane * 4, sm.lse[s]);
-      if (w == 1) load_to_lds<4>(dma_rsrc(Dh + r0, (N - r0) * 4), lane * 4, sm.dd[s]);
+      if constexpr (VARLEN) {
+        const int nv = min(Nb - r0, BWD_BQ);
+        stage_rows<HD, BWD_BQ, 4, swz_both<HD>>(Qh + (size_t)r0 * rs_q, rs_q, nv, sm.q[s], w, lane);
+        stage_rows<HD, BWD_BQ, 4, swz_both<HD>>(dOh + (size_t)r0 * rs_q, rs_q, nv, sm.dO[s], w, lane);
+        if (w == 0) load_to_lds<4>(dma_rsrc(LSEh + r0, nv * 4), lane * 4, sm.lse[s]);
+        if (w == 1) load_to_lds<4>(dma_rsrc(Dh + r0, nv * 4), lane * 4, sm.dd[s]);
+      } else {
+        stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(Qh, r0, N, sm.q[s], w, lane);
+        stage_tile<HD, BWD_BQ, 4, swz_both<HD>>(dOh, r0, N, sm.dO[s], w, lane);
+        if (w == 0) load_to_lds<4>(dma_rsrc(LSEh + r0, (N - r0) * 4), lane * 4, sm.lse[s]);
+        if (w == 1) load_to_lds<4>(dma_rsrc(Dh + r0, (N - r0) * 4), lane * 4, sm.dd[s]);
+      }
     };
     // Barrier between the two steps of tile t: this wave's loads of tile t+1 have landed and every
     // wave's reads of tile t-1 have returned; then tile t+2 goes into tile t-1's stage.
@@ -217,11 +242,19 @@ __device__ __forceinline__ void bwd_dkdv_job(
     // The group's query heads run one after another over the same K/V rows; dK and dV accumulate
     // across them in registers, so each element is still written once.
     for (int j = 0; j < group; ++j) {
-      const size_t qrows = (size_t)b * H + (size_t)hk * group + j;
-      Qh = Q + qrows * N * HD;
-      dOh = dO + qrows * N * HD;
-      LSEh = LSE2 + qrows * N;  // LSE * log2 e, written by the dQ kernel (or the fused forward)
-      Dh = Dg + qrows * N;
+      if constexpr (VARLEN) {
+        const size_t h = (size_t)hk * group + j;
+        Qh = Q + ((size_t)start * H + h) * HD;
+        dOh = dO + ((size_t)start * H + h) * HD;
+        LSEh = LSE2 + h * T + start;
+        Dh = Dg + h * T + start;
+      } else {
+        const size_t qrows = (size_t)b * H + (size_t)hk * group + j;
+        Qh = Q + qrows * N * HD;
+        dOh = dO + qrows * N * HD;
+        LSEh = LSE2 + qrows * N;  // LSE * log2 e, written by the dQ kernel (or the fused forward)
+        Dh = Dg + qrows * N;
+      }
       // Every wave has finished reading the previous head's tiles before this head's prologue
       // writes LDS.
       if (j > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -276,9 +309,9 @@ __device__ __forceinline__ void bwd_dkdv_job(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = kw0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (kr < N) {
-          dK[head + (size_t)kr * HD + 32 * cb + l32] = dk[cb][r] * scale;
-          dV[head + (size_t)kr * HD + 32 * cb + l32] = dv[cb][r];
+        if (kr < Nb) {
+          dK[head + (size_t)kr * rs_kv + 32 * cb + l32] = dk[cb][r] * scale;
+          dV[head + (size_t)kr * rs_kv + 32 * cb + l32] = dv[cb][r];
         }
       }
     }
@@ -297,13 +330,15 @@ struct DqSmem {
 // mask), with the workgroup's LDS stages `sm`.
 // ROW_TERMS: the job also computes its rows' D_i = sum_c dO[i,c] O[i,c] from O (bf16) and dO, and
 // writes D and LSE * log2 e (what the key-major job streams) to Dg and L2; otherwise it reads D
-// from Dg.
-template <int HD, bool CAUSAL, bool ROW_TERMS = false>
+// from Dg. Row layouts (dense or, with VARLEN, packed by cu_seqlens) are those of the key-major job;
+// LSE, Dg and L2 are [B, H, N] or [H, T].
+template <int HD, bool CAUSAL, bool ROW_TERMS = false, bool VARLEN = false>
 __device__ __forceinline__ void bwd_dq_job(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dg,
     float* __restrict__ dQ, int H, int group, int N, int n_qtiles, float scale, float scale_log2,
-    DqSmem<HD>& sm, int item, const bf16* __restrict__ O = nullptr, float* __restrict__ L2 = nullptr) {
+    DqSmem<HD>& sm, int item, const bf16* __restrict__ O = nullptr, float* __restrict__ L2 = nullptr,
+    const int32_t* __restrict__ cu_seqlens = nullptr, int T = 0) {
   constexpr int KSTEPS = HD / 16;
   constexpr int CBLK = HD / 32;
 
@@ -316,24 +351,39 @@ __device__ __forceinline__ void bwd_dq_job(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
+  int Nb = N, start = 0;  // this sequence's rows and (packed) first row
+  if constexpr (VARLEN) {
+    const int b = bh / H;
+    start = min(max(cu_seqlens[b], 0), T);
+    const int end = min(max(cu_seqlens[b + 1], start), T);
+    Nb = min(end - start, N);
+  }
+  const int rs_q = VARLEN ? H * HD : HD;                // element distance between query rows
+  const int rs_kv = VARLEN ? (H / group) * HD : HD;     // ... and between key rows
+  // A ragged batch pairs the tiles of the sequence's own tile count (the grid covers the longest).
+  const int nq = VARLEN ? (Nb + 127) / 128 : n_qtiles;
+  if (VARLEN && pair >= (CAUSAL ? (nq + 1) / 2 : nq)) return;  // no tile of this sequence left
+
   // Causal work per query tile grows with its index: a causal workgroup takes the query tiles
   // (n - 1 - p, p) one after the other and every workgroup carries the same work.
   for (int rep = 0; rep < (CAUSAL ? 2 : 1); ++rep) {
-    const int qt = CAUSAL && rep == 0 ? n_qtiles - 1 - pair : pair;
-    if (rep == 1 && qt == n_qtiles - 1 - pair) break;  // odd tile count: the middle tile runs once
+    const int qt = CAUSAL && rep == 0 ? nq - 1 - pair : pair;
+    if (rep == 1 && qt == nq - 1 - pair) break;  // odd tile count: the middle tile runs once
     // every wave is done with the first tile's LDS stages
     if (rep == 1) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const size_t head = (size_t)bh * N * HD;  // Q, dO, dQ rows of this query head
-    const size_t rowbase = (size_t)bh * N;
-    const size_t kv_head = ((size_t)(bh / H) * (H / group) + (bh % H) / group) * N * HD;
+    // Q, dO, dQ rows of this query head; its LSE/D rows; the K, V rows of its KV head
+    const size_t head = VARLEN ? ((size_t)start * H + bh % H) * HD : (size_t)bh * N * HD;
+    const size_t rowbase = VARLEN ? (size_t)(bh % H) * T + start : (size_t)bh * N;
+    const size_t kv_head = VARLEN ? ((size_t)start * (H / group) + (bh % H) / group) * HD
+                                  : ((size_t)(bh / H) * (H / group) + (bh % H) / group) * N * HD;
     const int q0 = qt * 128 + w * 32;
     const int qi = q0 + l32;
 
     bf16x8 qf[KSTEPS], df[KSTEPS];
     float lse2 = 0.f, Dq = 0.f;  // rows past N: Q = dO = 0 gives dS = 0
-    if (qi < N) {
-      const bf16x8* qs = reinterpret_cast<const bf16x8*>(Q + head + (size_t)qi * HD);
-      const bf16x8* ds = reinterpret_cast<const bf16x8*>(dO + head + (size_t)qi * HD);
+    if (qi < Nb) {
+      const bf16x8* qs = reinterpret_cast<const bf16x8*>(Q + head + (size_t)qi * rs_q);
+      const bf16x8* ds = reinterpret_cast<const bf16x8*>(dO + head + (size_t)qi * rs_q);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         qf[kk] = qs[2 * kk + g];
@@ -342,7 +392,7 @@ __device__ __forceinline__ void bwd_dq_job(
       lse2 = LSE[rowbase + qi] * kLog2e;
       if constexpr (ROW_TERMS) {
         // This lane's half of the row (chunks 2kk + g, as qf and df).
-        const bf16x8* os = reinterpret_cast<const bf16x8*>(O + head + (size_t)qi * HD);
+        const bf16x8* os = reinterpret_cast<const bf16x8*>(O + head + (size_t)qi * rs_q);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
           const bf16x8 a = os[2 * kk + g];
@@ -358,7 +408,7 @@ __device__ __forceinline__ void bwd_dq_job(
     }
     if constexpr (ROW_TERMS) {
       Dq += __shfl_xor(Dq, 32, 64);  // the other half of the row (lane l32 + 32)
-      if (qi < N && g == 0) {
+      if (qi < Nb && g == 0) {
         Dg[rowbase + qi] = Dq;
         L2[rowbase + qi] = lse2;  // the row's LSE in log2 units, streamed by the key-major job
       }
@@ -376,12 +426,18 @@ __device__ __forceinline__ void bwd_dq_job(
     const bf16* Vh = V + kv_head;
 
     auto stage = [&](int t, int s) {
-      stage_tile<HD, BWD_BK, 4, swz_both<HD>>(Kh, t * BWD_BK, N, sm.k[s], w, lane);
-      stage_tile<HD, BWD_BK, 4, swz_rows<HD>>(Vh, t * BWD_BK, N, sm.v[s], w, lane);
+      if constexpr (VARLEN) {
+        const size_t off = (size_t)t * BWD_BK * rs_kv;
+        stage_rows<HD, BWD_BK, 4, swz_both<HD>>(Kh + off, rs_kv, Nb - t * BWD_BK, sm.k[s], w, lane);
+        stage_rows<HD, BWD_BK, 4, swz_rows<HD>>(Vh + off, rs_kv, Nb - t * BWD_BK, sm.v[s], w, lane);
+      } else {
+        stage_tile<HD, BWD_BK, 4, swz_both<HD>>(Kh, t * BWD_BK, N, sm.k[s], w, lane);
+        stage_tile<HD, BWD_BK, 4, swz_rows<HD>>(Vh, t * BWD_BK, N, sm.v[s], w, lane);
+      }
     };
 
-    const int q_end = min(N, qt * 128 + 128);
-    const int n_kt = CAUSAL ? (q_end + BWD_BK - 1) / BWD_BK : (N + BWD_BK - 1) / BWD_BK;
+    const int q_end = min(Nb, qt * 128 + 128);
+    const int n_kt = CAUSAL ? (q_end + BWD_BK - 1) / BWD_BK : (Nb + BWD_BK - 1) / BWD_BK;
     // One key tile from LDS stage s; MASK applies the causal mask, needed only on the last two key
     // tiles: every key of a tile below them precedes the workgroup's first query (n_kt - 2 <= 2 qt).
     auto tile = [&](int s, int t, auto MASK_) {
@@ -428,8 +484,8 @@ __device__ __forceinline__ void bwd_dq_job(
     for (; t < t_mask; ++t) tile(t & 1, t, NoMask{});
     for (; t < n_kt; ++t) tile(t & 1, t, Mask{});
 
-    if (qi < N) {
-      float* out = dQ + head + (size_t)qi * HD;
+    if (qi < Nb) {
+      float* out = dQ + head + (size_t)qi * rs_q;
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) {
 #pragma unroll

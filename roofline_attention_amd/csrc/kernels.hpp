@@ -64,6 +64,13 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, float* dq, float* dk, float* dv,
                       int B, int H, int H_kv, int N, int d, bool causal, float scale, void* ws,
                       hipStream_t stream);
+// Ragged backward over packed rows (layouts of launch_fwd_bf16_varlen; lse [H, T]); the
+// workspace holds D and LSE * log2 e as [H, T] each.
+size_t bwd_varlen_workspace_bytes(int T, int H, int d);
+hipError_t launch_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, float* dq, float* dk, float* dv, const int32_t* cu_seqlens, int B,
+                             int max_seqlen, int T, int H, int H_kv, int d, bool causal, float scale, void* ws,
+                             hipStream_t stream);
 
 // Forward and backward in one cooperative launch: o, lse from the forward and dq, dk, dv from the
 // backward, with the workspace holding D, LSE * log2 e and an item counter.

@@ -97,6 +97,26 @@ __device__ __forceinline__ void stage_tile(const bf16* __restrict__ src, int row
   }
 }
 
+// Stages ROWS x HD bf16 rows of a matrix whose rows lie `rs` elements apart (packed [T, heads, HD]
+// token rows: rs = heads * HD) into an LDS tile with swizzle SWZ. `src` is the tile's first row;
+// only the first n_valid rows are read (the resource ends at the last of them), the others read as
+// zero. Called by all NWAVES waves of the workgroup, as stage_tile.
+template <int HD, int ROWS, int NWAVES, int (*SWZ)(int)>
+__device__ __forceinline__ void stage_rows(const bf16* __restrict__ src, int rs, int n_valid, bf16* tile, int w,
+                                           int lane) {
+  constexpr int CH = HD / 8;
+  constexpr int RPI = 1024 / (HD * 2);
+  constexpr int BLOCKS = ROWS / RPI;
+  static_assert(BLOCKS % NWAVES == 0, "tile geometry");
+  const u32x4 rsrc = dma_rsrc(src, n_valid > 0 ? (min(n_valid, ROWS) - 1) * rs * 2 + HD * 2 : 0);
+#pragma unroll
+  for (int u = 0; u < BLOCKS / NWAVES; ++u) {
+    const int blk = u * NWAVES + w;
+    const int row = blk * RPI + lane / CH;
+    load_to_lds<16>(rsrc, (row * rs + (((lane % CH) ^ SWZ(row)) * 8)) * 2, tile + blk * RPI * HD);
+  }
+}
+
 // Address of the 16-byte chunk `chunk` of row `row` in a tile with swizzle SWZ.
 template <int HD, int (*SWZ)(int)>
 __device__ __forceinline__ const bf16* tile_chunk(const bf16* tile, int row, int chunk) {

@@ -149,8 +149,9 @@ def make_prefill(w: Workload, with_dout: Optional[bool] = None) -> dict:
     return t
 
 
-def make_varlen(w: Workload, lengths=None) -> dict:
-    """Packed ragged batch: q [T,H,d], k/v [T,H_kv,d], cu_seqlens [B+1] int32, lengths [B].
+def make_varlen(w: Workload, lengths=None, with_dout: bool = False) -> dict:
+    """Packed ragged batch: q [T,H,d], k/v [T,H_kv,d], cu_seqlens [B+1] int32, lengths [B], and
+    with_dout an upstream gradient "do" [T,H,d].
 
     Lengths come from the kv-length stream (inclusive [kv_lo, kv_hi]) unless given; the rows of
     sequence b and head h are the (b, h) block of each tensor's streams, placed at rows
@@ -164,7 +165,9 @@ def make_varlen(w: Workload, lengths=None) -> dict:
     dt = torch_dtype(w.dtype)
     out = {}
     for name, tid, heads, factor in (("q", TENSOR_Q, w.H, w.qk_factor), ("k", TENSOR_K, w.H_kv, w.qk_factor),
-                                     ("v", TENSOR_V, w.H_kv, 1.0)):
+                                     ("v", TENSOR_V, w.H_kv, 1.0), ("do", TENSOR_DO, w.H, 1.0)):
+        if name == "do" and not with_dout:
+            continue
         t = torch.empty((T, heads, w.d), dtype=dt)
         for b in range(len(lengths)):
             for h in range(heads):

@@ -41,7 +41,7 @@ def test_binding_signatures_cover_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 5
+    assert lib.attn_abi_version() == 6
     assert lib.attn_status_string(OK) == b"ATTN_OK"
     assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
     assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
@@ -131,6 +131,32 @@ def test_fwd_varlen_validation(lib):
     assert call(cu=ctypes.c_void_p(BASE + 5 * GAP + 2)) == INVALID  # misaligned offsets
     assert call(lse=ctypes.c_void_p(BASE + 3 * GAP + 64)) == INVALID  # lse inside o
     assert call(T=0) == OK  # no rows: nothing is launched
+
+
+def test_bwd_varlen_validation(lib):
+    p = [addr(i) for i in range(11)]
+    T, H, d = 250, 4, 128
+    need = lib.attn_bwd_varlen_workspace_size(T, H, d)
+    assert need == 2 * H * T * 4  # D and LSE * log2 e per (head, token) row
+
+    def call(B=3, max_seqlen=100, T=T, H=H, H_kv=2, d=d, dtype=BF16, cu=p[9], ws=p[10], ws_bytes=need, lse=p[5]):
+        return lib.attn_bwd_varlen(p[0], p[1], p[2], p[3], p[4], lse, p[6], p[7], p[8], cu, B, max_seqlen, T, H,
+                                   H_kv, d, 1, 0.088, dtype, ws, ws_bytes, None)
+
+    assert call(cu=None) == INVALID
+    assert call(lse=None) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(B=0) == INVALID
+    assert call(max_seqlen=0) == INVALID
+    assert call(H=4, H_kv=3) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(cu=ctypes.c_void_p(BASE + 9 * GAP + 2)) == INVALID  # misaligned offsets
+    assert call(ws=ctypes.c_void_p(BASE + 6 * GAP + 64)) == INVALID  # workspace inside dq
+    assert call(lse=ctypes.c_void_p(BASE + 7 * GAP)) == INVALID  # lse (an input) is dk (an output)
+    assert call(T=0, ws=None, ws_bytes=0) == OK  # no rows: nothing is launched
 
 
 def test_decode_validation(lib):

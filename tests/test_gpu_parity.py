@@ -394,6 +394,84 @@ def test_fwdbwd_4k_causal_sampled_heads(lib):
         assert torch.isfinite(x).all()
 
 
+# ------------------------------------------------------------------- ragged backward ----
+
+def varlen_bwd_case(lib, w, lengths=None):
+    t = I.make_varlen(w, lengths, with_dout=True)
+    q, k, v, do, cu = dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["do"]), dev(t["cu_seqlens"])
+    max_len = int(max(t["lengths"].max(), 1))
+    o, lse = lib.fwd_varlen(q, k, v, cu, max_len, w.causal, w.scale)
+    dq, dk, dv = lib.bwd_varlen(q, k, v, o, do, lse, cu, max_len, w.causal, w.scale)
+    torch.cuda.synchronize()
+    return t, o.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv,d", [(4, 2, 128), (4, 4, 64), (8, 1, 128)])
+def test_bwd_varlen_ragged_lengths(lib, H, H_kv, d, causal):
+    # lengths straddling the 64/128-row tiles: 1, one short of, at and past a tile edge, and more
+    w = I.Workload("vlb", "varlen", 5, H, H_kv, 600, d, "bf16", causal, seed=24)
+    t, o, dq, dk, dv = varlen_bwd_case(lib, w, lengths=[1, 255, 256, 257, 600])
+    rdq, rdk, rdv, ro, _ = orc.attention_bwd_varlen(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]),
+                                                    t["cu_seqlens"].numpy(), causal, w.scale)
+    errs = [max_err(o, ro), max_err(dq, rdq), max_err(dk, rdk), max_err(dv, rdv)]
+    assert max(errs) <= TOL_BF16, errs
+
+
+def test_bwd_varlen_empty_sequences(lib):
+    w = I.Workload("vlb0", "varlen", 4, 4, 2, 700, 128, "bf16", True, seed=25)
+    t, o, dq, dk, dv = varlen_bwd_case(lib, w, lengths=[0, 700, 0, 3])
+    rdq, rdk, rdv, _, _ = orc.attention_bwd_varlen(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]),
+                                                   t["cu_seqlens"].numpy(), True, w.scale)
+    errs = [max_err(dq, rdq), max_err(dk, rdk), max_err(dv, rdv)]
+    assert max(errs) <= TOL_BF16, errs
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_equal_lengths_match_dense_bitwise(lib, causal):
+    # Equal lengths through both layouts: every gradient element comes from the same arithmetic in
+    # the same order (only the row strides and the work-item order differ), so the results match
+    # bit for bit.
+    B, H, H_kv, N, d = 3, 4, 2, 333, 128
+    w = I.Workload("vlbd", "varlen", B, H, H_kv, N, d, "bf16", causal, seed=26)
+    t, o, dq, dk, dv = varlen_bwd_case(lib, w, lengths=[N] * B)
+    dense = lambda x, h: dev(x.view(B, N, h, d).permute(0, 2, 1, 3).contiguous())
+    q, k, v, do = dense(t["q"], H), dense(t["k"], H_kv), dense(t["v"], H_kv), dense(t["do"], H)
+    od, ld = lib.fwd(q, k, v, causal, w.scale)
+    gd = lib.bwd(q, k, v, od, do, ld, causal, w.scale)
+    packed = lambda x, h: x.view(B, N, h, d).permute(0, 2, 1, 3)
+    assert torch.equal(packed(o, H), od.cpu())
+    for got, ref, h in zip((dq, dk, dv), gd, (H, H_kv, H_kv)):
+        assert torch.equal(packed(got, h), ref.cpu())
+
+
+def test_bwd_varlen_full_workload_sampled_sequences(lib):
+    # The ragged prefill workload (16 sequences of 512-8192 tokens, H 32 / H_kv 8, causal): the
+    # gradients of whole sequences and KV groups, which the oracle computes on those rows alone.
+    w = I.WORKLOADS["prefill_varlen"]
+    t, o, dq, dk, dv = varlen_bwd_case(lib, w)
+    cu, lengths = t["cu_seqlens"].numpy(), t["lengths"]
+    g = w.H // w.H_kv
+    order = np.argsort(lengths)
+    picks = [(int(order[0]), hk) for hk in range(w.H_kv)]  # the shortest sequence, every KV group
+    mid = int(order[min(np.searchsorted(lengths[order], 4096), len(order) - 1)])  # near 4096 tokens
+    picks += [(mid, 0), (mid, w.H_kv - 1)]
+    worst = [0.0] * 3
+    for b, hk in picks:
+        r = slice(int(cu[b]), int(cu[b + 1]))
+        hq = slice(hk * g, (hk + 1) * g)
+        sub = lambda x, hs: f64(x[r, hs])
+        rdq, rdk, rdv, _, _ = orc.attention_bwd_varlen(sub(t["q"], hq), sub(t["k"], slice(hk, hk + 1)),
+                                                       sub(t["v"], slice(hk, hk + 1)), sub(t["do"], hq),
+                                                       [0, r.stop - r.start], True, w.scale)
+        errs = [max_err(dq[r, hq], rdq), max_err(dk[r, hk:hk + 1], rdk), max_err(dv[r, hk:hk + 1], rdv)]
+        worst = [max(a, e) for a, e in zip(worst, errs)]
+    print(f"prefill_varlen bwd: sequences {sorted({b for b, _ in picks})}, max|ddQ|,|ddK|,|ddV| = {worst}")
+    assert max(worst) <= TOL_BF16, worst
+    for x in (dq, dk, dv):
+        assert torch.isfinite(x).all()
+
+
 def test_bwd_is_deterministic(lib):
     w = I.Workload("bdet", "fwdbwd", 1, 4, 4, 384, 128, "bf16", True, seed=19)
     t = I.make_prefill(w, with_dout=True)
