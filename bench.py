@@ -257,8 +257,8 @@ def main():
 
 def run_legs(torch, lib, I, L, reps=20):
     """Extra legs: the 4k prefill forward (causal and not; bf16, then fp8 inputs), the 1k causal
-    prefill, the step's forward+backward as one launch, the ragged prefill, GQA decode over a
-    contiguous and over a paged cache."""
+    prefill, the step's forward+backward as one launch, the ragged prefill and its backward, GQA
+    decode over a contiguous and over a paged cache."""
     legs = {}
     for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
         w = I.WORKLOADS[name]
@@ -317,10 +317,10 @@ def run_legs(torch, lib, I, L, reps=20):
     torch.cuda.empty_cache()
 
     w = I.WORKLOADS["prefill_varlen"]
-    t = I.make_varlen(w)
+    t = I.make_varlen(w, with_dout=True)
     lengths = t["lengths"]
     cu = t["cu_seqlens"].cuda()
-    t = {k: t[k].cuda() for k in ("q", "k", "v")}
+    t = {k: t[k].cuda() for k in ("q", "k", "v", "do")}
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.H, t["q"].shape[0]), dtype=torch.float32, device="cuda")
     max_len = int(lengths.max())
@@ -335,7 +335,23 @@ def run_legs(torch, lib, I, L, reps=20):
                               "sequences": int(len(lengths)), "max_len": max_len}
     log(f"[bench] leg prefill_varlen: {st['avg_ms']:.3f} ms, {legs['prefill_varlen']['tflops']:.1f} TFLOP/s "
         f"({int(lengths.sum())} tokens in {len(lengths)} sequences)")
-    del t, o, lse, cu
+
+    # The backward of the same ragged batch (attn_bwd_varlen: dQ kernel, then dK/dV kernel)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    g = dict(dq=torch.empty(t["q"].shape, **f32), dk=torch.empty(t["k"].shape, **f32),
+             dv=torch.empty(t["v"].shape, **f32))
+    wsv = torch.empty(lib.bwd_varlen_workspace_size(t["q"].shape[0], w.H, w.d), dtype=torch.uint8, device="cuda")
+    fn = lambda: lib.bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, cu, max_len, w.causal, w.scale,  # noqa
+                                workspace=wsv, **g)
+    warm_up(torch, fn)
+    wall, stats = time_region(torch, lib, fn, reps)
+    ms = sum(st["avg_ms"] for st in stats.values())
+    fl = sum(L.bwd_flops(1, w.H, int(n), w.d, w.causal) for n in lengths)
+    tf = fl / (ms * 1e-3) / 1e12
+    legs["prefill_varlen_bwd"] = {"kernels": {k: st["avg_ms"] for k, st in stats.items()}, "avg_ms": ms, "tflops": tf,
+                                  "frac_of_peak": tf / L.PEAK_BF16_TFLOPS, "wall_ms_per_call": wall / reps * 1e3}
+    log(f"[bench] leg prefill_varlen_bwd: {ms:.3f} ms, {tf:.1f} TFLOP/s (two kernels)")
+    del t, o, lse, cu, g, wsv
     torch.cuda.empty_cache()
 
     w = I.WORKLOADS["decode_gqa"]
