@@ -63,3 +63,45 @@ def test_graph_replays_match_eager(lib):
         torch.cuda.synchronize()
         for name in bufs:
             assert torch.equal(bufs[name], eager[name]), (rep, name)
+
+
+def test_ragged_graph_replays_match_eager(lib):
+    # The ragged forward and backward (device offsets read inside the kernels) under capture.
+    w = I.Workload("graph_vl", "varlen", 4, 4, 2, 600, 128, "bf16", True, seed=29)
+    t = I.make_varlen(w, lengths=[1, 600, 257, 130], with_dout=True)
+    q, k, v, do, cu = (t[n].cuda() for n in ("q", "k", "v", "do", "cu_seqlens"))
+    T = q.shape[0]
+    f32 = dict(dtype=torch.float32, device="cuda")
+    ws = torch.empty(lib.bwd_varlen_workspace_size(T, w.H, w.d), dtype=torch.uint8, device="cuda")
+
+    def new_bufs():
+        return {"o": torch.empty_like(q), "lse": torch.empty((w.H, T), **f32), "dq": torch.empty(q.shape, **f32),
+                "dk": torch.empty(k.shape, **f32), "dv": torch.empty(v.shape, **f32)}
+
+    def calls(b):
+        lib.fwd_varlen(q, k, v, cu, 600, True, w.scale, out=b["o"], lse=b["lse"])
+        lib.bwd_varlen(q, k, v, b["o"], do, b["lse"], cu, 600, True, w.scale, dq=b["dq"], dk=b["dk"], dv=b["dv"],
+                       workspace=ws)
+
+    eager = new_bufs()
+    calls(eager)
+    torch.cuda.synchronize()
+    bufs = new_bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(bufs)
+    for rep in range(3):
+        for x in bufs.values():
+            x.fill_(float("nan"))
+        calls(new_bufs())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in bufs:
+            assert torch.equal(bufs[name], eager[name]), (rep, name)

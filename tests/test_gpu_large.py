@@ -146,6 +146,38 @@ def test_varlen_fwd_past_4gib(lib):
     release()
 
 
+def test_varlen_bwd_past_4gib(lib):
+    # The ragged backward over packed [T, 1, 128] rows, T > 2^24: bf16 inputs past 4 GiB, fp32
+    # gradients past 8 GiB.
+    H, d = 1, 128
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([180, 0])))
+    lens = g.integers(256, 768, size=34000, endpoint=True)
+    lens[0], lens[-1] = 5, 700
+    T = int(lens.sum())
+    while T * H * d * 2 <= 4 * GIB + (1 << 20):
+        lens = np.concatenate([lens, [384]])
+        T = int(lens.sum())
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    scale = 1.0 / math.sqrt(d)
+    print(f"large varlen bwd: T={T}, B={len(lens)}", flush=True)
+    q, k, v, do = (torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(4))
+    for i, t in enumerate((q, k, v, do)):
+        fill_normal(t, 190 + i, 0.5 if i < 2 else 1.0, chunk_rows=1 << 20)
+    cud = torch.from_numpy(cu).cuda()
+    ml = int(lens.max())
+    o, lse = lib.fwd_varlen(q, k, v, cud, ml, True, scale)
+    dq, dk, dv = lib.bwd_varlen(q, k, v, o, do, lse, cud, ml, True, scale)
+    torch.cuda.synchronize()
+    for s in (0, len(lens) // 2, len(lens) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        rdq, rdk, rdv, _, _ = orc.attention_bwd_varlen(f64(q[a:e]), f64(k[a:e]), f64(v[a:e]), f64(do[a:e]),
+                                                       [0, e - a], True, scale)
+        for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
+            assert max_err(got[a:e], ref) <= TOL_BF16, s
+    del q, k, v, do, o, lse, dq, dk, dv, cud
+    release()
+
+
 def test_decode_cache_past_4gib(lib):
     # [5, 8, 2^19, 128] bf16 caches: 5 GiB each; sequence 4's rows start at 4 GiB.
     B, H, H_kv, N_cap, d = 5, 32, 8, 1 << 19, 128

@@ -472,6 +472,57 @@ def test_bwd_varlen_full_workload_sampled_sequences(lib):
         assert torch.isfinite(x).all()
 
 
+def test_varlen_malformed_offsets_stay_in_bounds(lib):
+    # Offsets that decrease, pass T or go negative are clamped on the device, so the kernels read
+    # and write only inside the tensors. Sequence 0 owns rows 0..149 alone (sequence 2, clamped to
+    # rows 150..699, overlaps its tail; sequences 1 and 3 clamp to empty): O, LSE and dQ of those
+    # rows depend on no other row's results and stay exact. (dK, dV of its keys also use query rows
+    # 150..199, whose O and LSE both sequences write.)
+    H, H_kv, d, T = 4, 2, 128, 700
+    w = I.Workload("vlbad", "varlen", 2, H, H_kv, 600, d, "bf16", True, seed=27)
+    t = I.make_varlen(w, lengths=[200, 500], with_dout=True)
+    q, k, v, do = dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["do"])
+    cu = torch.tensor([0, 200, 150, 900, -5], dtype=torch.int32, device="cuda")
+    o, lse = lib.fwd_varlen(q, k, v, cu, 600, True, w.scale)
+    dq, dk, dv = lib.bwd_varlen(q, k, v, o, do, lse, cu, 600, True, w.scale)
+    torch.cuda.synchronize()
+    r = slice(0, 150)
+    rdq, _, _, ro, rl = orc.attention_bwd_varlen(f64(t["q"][:200]), f64(t["k"][:200]), f64(t["v"][:200]),
+                                                 f64(t["do"][:200]), [0, 200], True, w.scale)
+    errs = [max_err(o[r].cpu(), ro[r]), max_err(lse[:, r].cpu(), rl[:, r]), max_err(dq[r].cpu(), rdq[r])]
+    assert max(errs) <= TOL_BF16, errs
+    for x in (o, dq, dk, dv):  # every row belongs to some clamped sequence and holds finite values
+        assert bool(torch.isfinite(x.float()).all())
+
+
+def test_varlen_max_seqlen_truncates_longer_sequences(lib):
+    # A sequence longer than max_seqlen is treated as its first max_seqlen rows; its other rows are
+    # not written. Sequence 0 (300 rows) runs as a 256-row sequence, sequence 1 (400 rows) as rows
+    # 300..555.
+    H, H_kv, d = 2, 1, 64
+    w = I.Workload("vltr", "varlen", 2, H, H_kv, 400, d, "bf16", False, seed=28)
+    t = I.make_varlen(w, lengths=[300, 400], with_dout=True)
+    q, k, v, do = dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["do"])
+    cu = dev(t["cu_seqlens"])
+    sentinel = 4096.0  # exact in bf16 and fp32
+    o = torch.full_like(q, sentinel)
+    o, lse = lib.fwd_varlen(q, k, v, cu, 256, False, w.scale, out=o)
+    dq = torch.full(q.shape, sentinel, dtype=torch.float32, device="cuda")
+    dk = torch.full(k.shape, sentinel, dtype=torch.float32, device="cuda")
+    dv = torch.full(v.shape, sentinel, dtype=torch.float32, device="cuda")
+    lib.bwd_varlen(q, k, v, o, do, lse, cu, 256, False, w.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for a, e in ((0, 256), (300, 556)):
+        r = slice(a, e)
+        rdq, rdk, rdv, ro, _ = orc.attention_bwd_varlen(f64(t["q"][r]), f64(t["k"][r]), f64(t["v"][r]),
+                                                        f64(t["do"][r]), [0, e - a], False, w.scale)
+        errs = [max_err(o[r].cpu(), ro), max_err(dq[r].cpu(), rdq), max_err(dk[r].cpu(), rdk),
+                max_err(dv[r].cpu(), rdv)]
+        assert max(errs) <= TOL_BF16, (a, errs)
+    for x in (o, dq, dk, dv):  # rows past each truncated sequence keep the sentinel
+        assert bool((x[256:300].float() == sentinel).all()) and bool((x[556:].float() == sentinel).all())
+
+
 def test_bwd_is_deterministic(lib):
     w = I.Workload("bdet", "fwdbwd", 1, 4, 4, 384, 128, "bf16", True, seed=19)
     t = I.make_prefill(w, with_dout=True)
