@@ -35,6 +35,8 @@ constexpr size_t fused_smem_bytes() {
   return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
+static_assert(FWD_THREADS == BWD_THREADS, "the fused kernel runs the forward job with the backward's workgroup");
+
 template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(BWD_THREADS, 1) void fwdbwd_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,

@@ -7,7 +7,7 @@ namespace ra {
 namespace {
 
 template <int HD, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(FWD_THREADS, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(FWD_THREADS, 8 / FWD_WAVES) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ cu_seqlens, int T, int H,
     int group, int N, int n_qtiles, float scale_log2, int split_pairs) {

@@ -41,9 +41,16 @@
 
 namespace ra {
 
-constexpr int FWD_BR = 128;
+#ifndef RA_FWD_WAVES
+#define RA_FWD_WAVES 4
+#endif
+// Waves per workgroup, 32 query rows each. Eight waves (one workgroup per CU sharing each K/V tile)
+// measured within 1% of four ([2,32,4096,128]: 482 vs 489 us non-causal, 271 vs 270 us causal,
+// where eight spill 13 registers), so four stay.
+constexpr int FWD_WAVES = RA_FWD_WAVES;
+constexpr int FWD_BR = 32 * FWD_WAVES;
 constexpr int FWD_BC = 64;
-constexpr int FWD_THREADS = 256;
+constexpr int FWD_THREADS = 64 * FWD_WAVES;
 constexpr float kLazyRescale = 8.0f;  // log2 units: P values stay below 2^8
 
 // LDS tiles: [2 stages][FWD_BC rows][HD] bf16, unpadded. The 16-byte chunk c of row r is stored
@@ -179,11 +186,11 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
 
     // Direct-to-LDS staging: wave w issues blocks w, w + 4, ... of a tile (RPI rows each). Lane i
     // fills row blk*RPI + i / CHUNKS at chunk position i % CHUNKS with global chunk
-    // position ^ swz(row). The swizzles repeat within 4*RPI rows, so a lane's byte offset moves by
+    // position ^ swz(row). The swizzles repeat within FWD_WAVES*RPI rows, so a lane's offset moves by
     // BLK_BYTES from one of its blocks to the next. The buffer resource of tile kt starts at its
     // first row and ends with the last byte of the tile's last row inside the sequence, so rows past
     // the sequence end load as zeros.
-    const int BLK_BYTES = 4 * RPI * rs_kv * 2;  // byte distance between this wave's blocks
+    const int BLK_BYTES = FWD_WAVES * RPI * rs_kv * 2;  // byte distance between this wave's blocks
     const int st_row = w * RPI + lane / CHUNKS;
     const int k_voff = (st_row * rs_kv + (((lane % CHUNKS) ^ swz_k<HD>(st_row)) * 8)) * 2;
     const int v_voff = (st_row * rs_kv + (((lane % CHUNKS) ^ swz_v<HD>(st_row)) * 8)) * 2;
@@ -194,15 +201,15 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       const int row0 = kt * FWD_BC;
       const u32x4 rsrc = dma_rsrc(k_head + (size_t)row0 * rs_kv, tile_bytes(row0));
 #pragma unroll
-      for (int u = 0; u < BLOCKS / 4; ++u)
-        load_to_lds<16>(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * 4 + w) * RPI * HD]);
+      for (int u = 0; u < BLOCKS / FWD_WAVES; ++u)
+        load_to_lds<16>(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * FWD_WAVES + w) * RPI * HD]);
     };
     auto issue_v = [&](int kt, int stage) {
       const int row0 = kt * FWD_BC;
       const u32x4 rsrc = dma_rsrc(v_head + (size_t)row0 * rs_kv, tile_bytes(row0));
 #pragma unroll
-      for (int u = 0; u < BLOCKS / 4; ++u)
-        load_to_lds<16>(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * 4 + w) * RPI * HD]);
+      for (int u = 0; u < BLOCKS / FWD_WAVES; ++u)
+        load_to_lds<16>(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * FWD_WAVES + w) * RPI * HD]);
     };
 
     // K A-operand read (S^T block kb, k-step kk): row 32kb + l32, chunk 2kk + g at position
