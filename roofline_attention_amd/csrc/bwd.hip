@@ -106,13 +106,9 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t dkdv_smem = sizeof(DkdvSmem<HD>);
-  static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
-  if (!attr_set) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<HD, CAUSAL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dkdv_smem);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_opt_in{0};  // devices this instantiation's limit is raised on
+  err = allow_dynamic_lds(lds_opt_in, reinterpret_cast<const void*>(&bwd_dkdv_kernel<HD, CAUSAL>), (int)dkdv_smem);
+  if (err != hipSuccess) return err;
   {
     TimedScope ts(dkdv_name, stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<HD, CAUSAL>), dim3(total_kv), dim3(BWD_THREADS), dkdv_smem, stream, Q, K,
@@ -145,13 +141,9 @@ hipError_t launch_varlen(const void* q, const void* k, const void* v, const void
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t dkdv_smem = sizeof(DkdvSmem<HD>);
-  static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
-  if (!attr_set) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_varlen_kernel<HD, CAUSAL>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dkdv_smem);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_opt_in{0};  // devices this instantiation's limit is raised on
+  err = allow_dynamic_lds(lds_opt_in, reinterpret_cast<const void*>(&bwd_dkdv_varlen_kernel<HD, CAUSAL>), (int)dkdv_smem);
+  if (err != hipSuccess) return err;
   {
     TimedScope ts(dkdv_name, stream);
     hipLaunchKernelGGL((bwd_dkdv_varlen_kernel<HD, CAUSAL>), dim3(total_kv), dim3(BWD_THREADS), dkdv_smem, stream,

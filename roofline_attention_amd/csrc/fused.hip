@@ -94,15 +94,11 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* dout,
   int* counter = reinterpret_cast<int*>(L2 + rows);
   const size_t smem = fused_smem_bytes<HD>();
   auto kernel = &fwdbwd_kernel<HD, CAUSAL>;
-  static bool attr_set = false;  // one dynamic-LDS opt-in per instantiation
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_opt_in{0};  // devices this instantiation's limit is raised on
+  hipError_t err = allow_dynamic_lds(lds_opt_in, reinterpret_cast<const void*>(kernel), (int)smem);
+  if (err != hipSuccess) return err;
   int dev = 0, per_cu = 0, cus = 0;
-  hipError_t err = hipGetDevice(&dev);
+  err = hipGetDevice(&dev);
   if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err == hipSuccess)
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel), BWD_THREADS,

@@ -37,13 +37,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   // A causal grid of pairs that fills fewer than two workgroups per CU runs each pair as two
   // workgroups (measured on [4,16,1024,64]: 335 -> 380 TFLOP/s; on grids that fill the chip the
   // pairs stay together: [2,32,4096,128] 825 vs 787).
-  static int cus = 0;  // CUs of the device (one device per process here), queried once
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess)
-      cus = 0;
-  }
+  const int cus = device_cus();
   const int split = CAUSAL && !VARLEN && cus > 0 && total < 2LL * cus ? 1 : 0;
   if (split) total *= 2;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;

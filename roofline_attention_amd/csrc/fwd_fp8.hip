@@ -360,13 +360,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   long long total = (long long)(CAUSAL ? (n_qt + 1) / 2 : n_qt) * H * B;
   // A causal grid of pairs that fills fewer than two workgroups per CU runs each pair as two
   // workgroups, as the bf16 forward does.
-  static int cus = 0;  // CUs of the device (one device per process here), queried once
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess)
-      cus = 0;
-  }
+  const int cus = device_cus();
   const int split = CAUSAL && cus > 0 && total < 2LL * cus ? 1 : 0;
   if (split) total *= 2;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -7,7 +7,32 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace ra {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` once per device (bit d of `done` marks device
+// d; the attribute is per device). Safe to call from several host threads: the call is idempotent
+// and the mark is atomic.
+inline hipError_t allow_dynamic_lds(std::atomic<uint64_t>& done, const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
+// Compute units of the current device, or 0 if the runtime cannot say.
+inline int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
 
 // Brackets one kernel launch with timing events when the opt-in timer is enabled.
 class TimedScope {
