@@ -20,7 +20,9 @@
  *   - d must be 64 or 128. N >= 1; N * d must not exceed 2^30.
  *   - Ownership: the caller allocates and frees every buffer, including workspaces. The library
  *     allocates no device memory, keeps no pointer after a call returns, and holds no state except
- *     the opt-in kernel timer below.
+ *     the opt-in kernel timer below and, per device, whether it has already raised a kernel's
+ *     dynamic-LDS limit (done on a kernel's first launch on that device). Calls from several host
+ *     threads may run concurrently, on different streams and buffers; the timer is the exception.
  *   - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
  *     returns without waiting. Faults inside a kernel surface at the caller's next synchronisation.
  *   - Errors: every argument check runs before any launch; a failing check enqueues nothing and
