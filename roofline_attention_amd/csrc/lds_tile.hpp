@@ -78,9 +78,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
 }
 
+// Bytes of the rows [row0, row0 + ROWS) of a [n_rows, HD] bf16 matrix that exist: the byte count
+// of a staged tile's buffer resource. Only the tile's own rows count, so the value is at most
+// ROWS * HD * 2 and never overflows int (n_rows * HD * 2 itself reaches 2^31 at n_rows * HD = 2^30,
+// the largest size the library accepts).
+template <int HD, int ROWS>
+__host__ __device__ constexpr int tile_span_bytes(int n_rows, int row0) {
+  return (n_rows - row0 <= 0 ? 0 : (n_rows - row0 < ROWS ? n_rows - row0 : ROWS)) * HD * 2;
+}
+static_assert(tile_span_bytes<128, 64>(1 << 23, 0) == 64 * 128 * 2, "first tile at N * d = 2^30");
+static_assert(tile_span_bytes<64, 64>(1 << 24, 0) == 64 * 64 * 2, "first tile at N * d = 2^30");
+static_assert(tile_span_bytes<128, 64>((1 << 23), (1 << 23) - 10) == 10 * 128 * 2, "ragged last tile");
+static_assert(tile_span_bytes<128, 64>(100, 128) == 0, "tile past the end");
+
 // Stages ROWS x HD bf16 rows [row0, row0 + ROWS) of a row-major [n_rows, HD] matrix into an LDS
 // tile with swizzle SWZ; rows at or beyond n_rows read as zero. Called by all NWAVES waves of
-// the workgroup, wave w issuing the 1 KB blocks w, w + NWAVES, ...
+// the workgroup, wave w issuing the 1 KB blocks w, w + NWAVES, ... The buffer resource covers
+// only the tile's own rows (tile_span_bytes).
 template <int HD, int ROWS, int NWAVES, int (*SWZ)(int)>
 __device__ __forceinline__ void stage_tile(const bf16* __restrict__ src, int row0, int n_rows, bf16* tile, int w,
                                            int lane) {
@@ -88,7 +102,7 @@ __device__ __forceinline__ void stage_tile(const bf16* __restrict__ src, int row
   constexpr int RPI = 1024 / (HD * 2);
   constexpr int BLOCKS = ROWS / RPI;
   static_assert(BLOCKS % NWAVES == 0, "tile geometry");
-  const u32x4 rsrc = dma_rsrc(src + (size_t)row0 * HD, (n_rows - row0) * HD * 2);
+  const u32x4 rsrc = dma_rsrc(src + (size_t)row0 * HD, tile_span_bytes<HD, ROWS>(n_rows, row0));
 #pragma unroll
   for (int u = 0; u < BLOCKS / NWAVES; ++u) {
     const int blk = u * NWAVES + w;
