@@ -227,6 +227,26 @@ attn_status attn_timing_reset(void);
 int attn_timing_count(void);
 attn_status attn_timing_get(int index, const char** name, long long* launches, double* total_ms);
 
+/*
+ * Per-launch durations behind attn_timing_get, so a harness can report a distribution (median and
+ * tail percentiles, "M4.2 - GPU Execution Model for Transformer Kernels", section 0x0B, Level 4)
+ * instead of one mean: writes the durations in milliseconds of the first min(cap, launches)
+ * launches of the index-th kernel name, in launch order, to ms[0..cap) (host memory owned by the
+ * caller) and returns the number of launches recorded since the last reset. Returns -1 on a bad
+ * index, on cap < 0, on ms == NULL with cap > 0, or on a HIP error (attn_last_error says which).
+ */
+int attn_timing_samples(int index, float* ms, int cap);
+
+/*
+ * Releases every HIP object the library has created: it disables the timer, waits for the events
+ * still pending and destroys all timing events (the only objects the library creates; it
+ * allocates no device memory). Meant for the end of a process, so that no library-owned runtime
+ * object is left to the HIP runtime's own teardown (where a tool that intercepts HIP calls, such
+ * as a profiler, may already have finalised). The library stays usable afterwards: a later timed
+ * launch creates events again. Not for concurrent use with timed launches.
+ */
+attn_status attn_release(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,7 @@ kernels; there is no fallback path: if the library is missing this module fails 
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import math
 import os
@@ -20,7 +21,7 @@ LIB_PATH = os.environ.get("ROOFATTN_LIB", os.path.join(_HERE, "libroofattn.so"))
 
 ATTN_F32, ATTN_BF16 = 0, 1
 # The ABI version these signatures describe (attn_abi_version() of the matching library).
-ABI_VERSION = 6
+ABI_VERSION = 7
 _DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
 
 # Every symbol include/attn.h declares, with (restype, argtypes).
@@ -50,6 +51,8 @@ SIGNATURES = {
     "attn_timing_count": (_I, []),
     "attn_timing_get": (_I, [_I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_longlong),
                              ctypes.POINTER(ctypes.c_double)]),
+    "attn_timing_samples": (_I, [_I, ctypes.POINTER(ctypes.c_float), _I]),
+    "attn_release": (_I, []),
 }
 
 
@@ -72,6 +75,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 
 _lib = load_library()
+
+
+def release() -> None:
+    """Destroys the library's timing events (attn_release); the library stays usable."""
+    _check(_lib.attn_release())
+
+
+# Python's exit handlers run before the C runtime's teardown (and before a profiler attached to the
+# process finalises), so no library-owned HIP object is left for that teardown.
+atexit.register(lambda: _lib.attn_release())
 
 
 def abi_version() -> int:
@@ -393,6 +406,23 @@ def timing_read() -> dict:
         ms = ctypes.c_double()
         _check(_lib.attn_timing_get(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)))
         out[name.value.decode()] = (n.value, ms.value)
+    return out
+
+
+def timing_samples() -> dict:
+    """{kernel name: [duration in ms of each launch, in launch order]} since the last reset."""
+    out = {}
+    for i in range(_lib.attn_timing_count()):
+        name = ctypes.c_char_p()
+        _check(_lib.attn_timing_get(i, ctypes.byref(name), None, None))
+        n = _lib.attn_timing_samples(i, None, 0)
+        if n < 0:
+            raise AttnError(_lib.attn_last_error().decode())
+        buf = (ctypes.c_float * max(n, 1))()
+        got = _lib.attn_timing_samples(i, buf, n)
+        if got < 0:
+            raise AttnError(_lib.attn_last_error().decode())
+        out[name.value.decode()] = [float(buf[j]) for j in range(min(got, n))]
     return out
 
 

@@ -65,6 +65,7 @@ struct TimerRecord {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
   long long launches = 0;
   double total_ms = 0.0;
+  std::vector<float> samples;  // duration of every drained launch, in launch order (ms)
 };
 
 std::mutex g_mu;
@@ -100,6 +101,7 @@ attn_status drain_locked() {
         return fail(ATTN_ERR_HIP, "event elapsed time failed");
       r.total_ms += ms;
       r.launches += 1;
+      r.samples.push_back(ms);
       g_free_events.push_back(pr.first);
       g_free_events.push_back(pr.second);
     }
@@ -131,7 +133,7 @@ TimedScope::~TimedScope() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 6; }
+int attn_abi_version(void) { return 7; }
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -429,6 +431,39 @@ attn_status attn_timing_reset(void) {
   attn_status st = drain_locked();
   g_records.clear();
   return st == ATTN_OK ? ok() : st;
+}
+
+int attn_timing_samples(int index, float* ms, int cap) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (index < 0 || index >= (int)g_records.size()) {
+    fail(ATTN_ERR_INVALID_ARG, "timer index out of range");
+    return -1;
+  }
+  if (cap < 0 || (cap > 0 && ms == nullptr)) {
+    fail(ATTN_ERR_INVALID_ARG, "ms must hold cap >= 0 floats");
+    return -1;
+  }
+  if (drain_locked() != ATTN_OK) return -1;
+  const std::vector<float>& v = g_records[index].samples;
+  const int n = (int)v.size();
+  for (int i = 0; i < n && i < cap; ++i) ms[i] = v[i];
+  ok();
+  return n;
+}
+
+attn_status attn_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_timing = false;
+  attn_status st = drain_locked();  // waits for every recorded event before it is destroyed
+  for (auto& r : g_records)
+    for (auto& pr : r.pending) g_free_events.push_back(pr.first), g_free_events.push_back(pr.second);
+  g_records.clear();
+  bool destroyed = true;
+  for (hipEvent_t e : g_free_events) destroyed = hipEventDestroy(e) == hipSuccess && destroyed;
+  g_free_events.clear();
+  g_free_events.shrink_to_fit();
+  if (st != ATTN_OK) return st;
+  return destroyed ? ok() : fail(ATTN_ERR_HIP, "hipEventDestroy failed");
 }
 
 int attn_timing_count(void) {

@@ -41,7 +41,7 @@ def test_binding_signatures_cover_the_header():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 6
+    assert lib.attn_abi_version() == 7
     assert lib.attn_status_string(OK) == b"ATTN_OK"
     assert lib.attn_status_string(WORKSPACE) == b"ATTN_ERR_WORKSPACE"
     assert lib.attn_status_string(99) == b"ATTN_ERR_UNKNOWN"
@@ -236,3 +236,12 @@ def test_timer_without_launches(lib):
     assert lib.attn_timing_reset() == OK
     assert lib.attn_timing_count() == 0
     assert lib.attn_timing_get(0, None, None, None) == INVALID
+    assert lib.attn_timing_samples(0, None, 0) == -1
+    assert lib.attn_timing_samples(-1, None, 0) == -1
+
+
+def test_release_without_launches_is_a_no_op(lib):
+    # no event was ever created: nothing to wait for or destroy, and no HIP call is made
+    assert lib.attn_release() == OK
+    assert lib.attn_release() == OK
+    assert lib.attn_timing_count() == 0
