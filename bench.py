@@ -2,14 +2,20 @@
 
 A step is one forward + backward pass (attn_fwd then attn_bwd, all forward and backward kernels)
 of causal bf16 attention over the [B=2, H=16, N=4096, d=128] synthetic batch, inputs resident in
-HBM before timing starts. The decode kernels and the two 4k prefill forwards are timed as extra
-legs in the same run and reported beside the step. Kernel durations come from HIP events that
-the library records on its launch stream around every kernel while its timer is enabled.
+HBM before timing starts. The decode kernels and the prefill forwards are timed as extra legs in
+the same run and reported beside the step. Kernel durations come from HIP events that the library
+records on its launch stream around every kernel while its timer is enabled; every timed call
+keeps its own sample, so each figure carries its median, p10, p90 and minimum ("M4.2 - GPU
+Execution Model for Transformer Kernels", section 0x0B, Level 4: report a median and a tail, not
+one timing). Rates are priced against the published MI355X peaks and against ceilings measured on
+the same GPU in the same run ("Why Fast GPUs Still Wait for Memory", section "pi is the top of a
+stack": measure your own ceilings before trusting them).
 
 Output: one JSON line on stdout (rank 0), with the roofline of the dominant kernel and the fp64
 CPU oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--legs/--no-legs]
+                       [--no-ceilings]
 """
 from __future__ import annotations
 
@@ -17,6 +23,7 @@ import argparse
 import json
 import os
 import platform
+import subprocess
 import sys
 import time
 
@@ -24,9 +31,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd/bwd TFLOP/s and decode HBM GB/s, % of MI355X roofline"
+WARMUP_S = 0.2  # untimed seconds of load before every timed region (the clock ramps up first)
+LEG_CALLS = 30  # timed calls per leg (>= 20 samples each)
+
+# Ceilings measured by the ceiling microbenchmarks (csrc/ceilings.hip) on one MI355X, used only when
+# the executable is not available in this run: dense bf16 and E4M3 MFMA on the full chip after a
+# warm-up, and the HBM streaming read.
+COMMITTED_CEILINGS = {"mfma_bf16_tflops": 2435.4, "mfma_fp8_tflops": 4907.0, "hbm_read_gbs": 7146.0}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -34,17 +48,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", dest="legs", action="store_true", default=True)
     ap.add_argument("--no-legs", dest="legs", action="store_false")
+    ap.add_argument("--no-ceilings", action="store_true", help="use the committed ceilings, do not measure them")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_stats(lib, before=None):
-    rec = lib.timing_read()
-    return {k: {"launches": n, "avg_ms": ms / n if n else None, "total_ms": ms} for k, (n, ms) in rec.items()}
+def dist(samples):
+    """Summary of per-call durations in ms: count, mean, median, p10, p90, min, max."""
+    import numpy as np
+    x = np.asarray(samples, dtype=np.float64)
+    if x.size == 0:
+        return {"n": 0}
+    return {"n": int(x.size), "mean_ms": float(x.mean()), "median_ms": float(np.median(x)),
+            "p10_ms": float(np.percentile(x, 10)), "p90_ms": float(np.percentile(x, 90)), "min_ms": float(x.min()),
+            "max_ms": float(x.max())}
 
 
 def calibration_copy(torch, nbytes=1 << 30):
@@ -84,9 +105,24 @@ def measured_traffic(kernel):
     return ent["hbm_bytes_per_launch"]
 
 
-def warm_up(torch, fn, seconds=0.2, min_calls=3):
-    """Untimed calls of fn() for at least `seconds` of wall time: after the host-side input setup
-    the GPU has idled and its clock ramps up again over the first tens of milliseconds of load."""
+def ceilings(measure: bool):
+    """MFMA and HBM ceilings of this GPU: measured now by the ceiling microbenchmarks (a child
+    process), or the committed values when measuring is off or the executable is missing."""
+    if measure:
+        try:
+            from roofline_attention_amd import ceilings as C
+            m = C.measure(timeout=180.0)
+            return {"source": "measured in this run (roofline_attention_amd/ceilings)",
+                    **{k: float(m[k]) for k in COMMITTED_CEILINGS}}
+        except (OSError, ValueError, KeyError, subprocess.SubprocessError) as e:
+            log(f"[bench] ceilings not measured ({type(e).__name__}: {e}); using the committed values")
+    return {"source": "committed measurement of the ceiling microbenchmarks on one MI355X", **COMMITTED_CEILINGS}
+
+
+def warm_up(torch, fn, seconds=WARMUP_S, min_calls=3):
+    """Untimed calls of fn() for at least `seconds` of wall time and at least `min_calls` calls:
+    after the host-side input setup the GPU has idled and its clock ramps up again over the first
+    tens of milliseconds of load."""
     t0 = time.perf_counter()
     n = 0
     while n < min_calls or time.perf_counter() - t0 < seconds:
@@ -98,25 +134,56 @@ def warm_up(torch, fn, seconds=0.2, min_calls=3):
     return n
 
 
-def time_region(torch, lib, fn, steps):
-    """Runs fn() `steps` times between synchronisations; returns (wall seconds, kernel stats)."""
+def time_calls(torch, lib, fn, calls, between=None):
+    """Runs fn() `calls` times back to back between two synchronisations, with the library's timer
+    on. Returns (wall seconds, {kernel: per-launch ms}, per-call ms). A call's duration is the time
+    between events recorded on the launch stream before and after it; `between`, if given, runs
+    before each call outside the timer and outside the call's events (e.g. a cache flush)."""
     lib.timing_reset()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
     lib.timing_enable(True)
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for e0, e1 in ev:
+        if between is not None:
+            lib.timing_enable(False)
+            between()
+            lib.timing_enable(True)
+        e0.record()
         fn()
+        e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lib.timing_enable(False)
-    stats = kernel_stats(lib)
+    per_kernel = lib.timing_samples()
     lib.timing_reset()
-    return t1 - t0, stats
+    per_call = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return t1 - t0, per_kernel, per_call
+
+
+def host_record():
+    """CPU model, sockets, NUMA nodes and the CPUs this process may run on."""
+    model, sockets = None, set()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name") and model is None:
+                    model = line.split(":", 1)[1].strip()
+                elif line.startswith("physical id"):
+                    sockets.add(line.split(":", 1)[1].strip())
+    except OSError:
+        pass
+    try:
+        numa = len([n for n in os.listdir("/sys/devices/system/node") if n.startswith("node") and n[4:].isdigit()])
+    except OSError:
+        numa = None
+    return {"cpu_model": model or platform.processor() or platform.machine(),
+            "sockets": len(sockets) or None, "numa_nodes": numa,
+            "affinity_cpus": len(os.sched_getaffinity(0)), "os_cpus": os.cpu_count()}
 
 
 def cpu_baseline(w, target_s):
     """The fp64 oracle's forward+backward on whole heads of the same workload until ~target_s elapse."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention as orc
@@ -135,7 +202,8 @@ def cpu_baseline(w, target_s):
         elapsed += time.perf_counter() - t0
         done += 1
     flops = done * (L.fwd_flops(1, 1, w.N, w.d, w.causal) + L.bwd_flops(1, 1, w.N, w.d, w.causal))
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in pools] or [1])
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
@@ -143,8 +211,23 @@ def cpu_baseline(w, target_s):
         "kind": "oracle",
         "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, fp64 numpy forward+backward "
                   f"with explicit S, {elapsed:.2f} s wall; algorithmic FLOPs (causal halved) / time",
-        "host": platform.processor() or platform.machine(),
+        "host": {**host_record(), "blas": sorted({p.get("internal_api", "?") for p in pools}),
+                 "blas_threads": int(threads)},
     }
+
+
+def rate_of(kind, amount, ms, ceil):
+    """Algorithmic rate of `amount` FLOPs or bytes done in `ms`, with its fractions of the published
+    peak and of the measured ceiling."""
+    from roofline_attention_amd import ledger as L
+    if kind == "mfma":
+        r = amount / (ms * 1e-3) / 1e12
+        return {"tflops": r, "frac_of_peak": r / L.PEAK_BF16_TFLOPS, "frac_of_ceiling": r / ceil["mfma_bf16_tflops"]}
+    if kind == "mfma8":
+        r = amount / (ms * 1e-3) / 1e12
+        return {"tflops": r, "frac_of_peak": r / L.PEAK_FP8_TFLOPS, "frac_of_ceiling": r / ceil["mfma_fp8_tflops"]}
+    r = amount / (ms * 1e-3) / 1e9
+    return {"gbs": r, "frac_of_peak": r / L.PEAK_HBM_GBS, "frac_of_ceiling": r / ceil["hbm_read_gbs"]}
 
 
 def main():
@@ -160,6 +243,8 @@ def main():
     from roofline_attention_amd import inputs as I
     from roofline_attention_amd import ledger as L
 
+    ceil = ceilings(not a.no_ceilings)
+    log(f"[bench] ceilings: {ceil}")
     torch.cuda.set_device(0)
     calibration_copy(torch)
     w = I.WORKLOADS["fwdbwd_4k_causal"]
@@ -176,11 +261,11 @@ def main():
         lib.fwd(q, k, v, w.causal, w.scale, out=o, lse=lse)
         lib.bwd(q, k, v, o, do, lse, w.causal, w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps")
-    wall, stats = time_region(torch, lib, step, a.steps)
+    t_w = time.perf_counter()
+    n_warm = warm_up(torch, step, seconds=WARMUP_S, min_calls=a.warmup)
+    warm_s = time.perf_counter() - t_w
+    log(f"[bench] warm-up {n_warm} steps in {warm_s:.2f} s; timing {a.steps} steps")
+    wall, per_kernel, per_step = time_calls(torch, lib, step, a.steps)
     ms_per_step = wall / a.steps * 1e3
     step_flops = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal) + L.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
     value = step_flops / (wall / a.steps) / 1e12
@@ -196,35 +281,29 @@ def main():
         "bwd_dq_d128_causal": ("mfma", 2.0 * Nsq),
     }
     kernels = {}
-    for name, st in stats.items():
+    for name, smp in per_kernel.items():
         kind, amount = work.get(name, (None, None))
-        ent = dict(st)
-        if kind == "mfma" and st["avg_ms"]:
-            ent["tflops"] = amount / (st["avg_ms"] * 1e-3) / 1e12
-            ent["frac_of_peak"] = ent["tflops"] / L.PEAK_BF16_TFLOPS
-        elif kind == "hbm" and st["avg_ms"]:
-            ent["gbs"] = amount / (st["avg_ms"] * 1e-3) / 1e9
-            ent["frac_of_peak"] = ent["gbs"] / L.PEAK_HBM_GBS
+        ent = {"launches": len(smp), **dist(smp)}
+        if kind is not None:
+            ent["avg_ms"] = ent["mean_ms"]
+            ent.update(rate_of(kind, amount, ent["mean_ms"], ceil))
+            ent["at_median"] = rate_of(kind, amount, ent["median_ms"], ceil)
         kernels[name] = ent
-    dom = max(stats, key=lambda n: stats[n]["total_ms"])
+    dom = max(per_kernel, key=lambda n: sum(per_kernel[n]))
     kind, amount = work[dom]
-    avg_s = stats[dom]["avg_ms"] * 1e-3
-    if kind == "mfma":
-        roof = {"kernel": dom, "bound": "mfma", "achieved": amount / avg_s / 1e12, "peak": L.PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": amount / avg_s / 1e9, "peak": L.PEAK_HBM_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom)
-    roof["avg_ms"] = stats[dom]["avg_ms"]
-    roof["algorithmic_per_launch"] = amount
+    d = kernels[dom]
+    roof = {"kernel": dom, "bound": "mfma", "achieved": d["tflops"], "peak": L.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": d["frac_of_peak"], "traffic": measured_traffic(dom),
+            "ceiling": ceil["mfma_bf16_tflops"], "frac_of_ceiling": d["frac_of_ceiling"],
+            "avg_ms": d["mean_ms"], "median_ms": d["median_ms"], "p10_ms": d["p10_ms"], "p90_ms": d["p90_ms"],
+            "min_ms": d["min_ms"], "algorithmic_per_launch": amount,
+            "samples_ms": [round(x, 5) for x in per_kernel[dom]]}
 
     legs = {}
     if a.legs:
         del q, k, v, do, o, lse, dq, dk, dv, ws, t
         torch.cuda.empty_cache()
-        legs = run_legs(torch, lib, I, L)
+        legs = run_legs(torch, lib, I, L, ceil)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -238,7 +317,11 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "warmup_calls": n_warm,
+        "warmup_s": warm_s,
         "ms_per_step": ms_per_step,
+        "step_device_ms": dist(per_step),
+        "step_samples_ms": [round(x, 5) for x in per_step],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -249,31 +332,46 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "kernels": kernels,
         "legs": legs,
     }
     print(json.dumps(out), flush=True)
 
 
-def run_legs(torch, lib, I, L, reps=20):
+def leg_record(per_kernel, per_call, wall, calls, kind, amount, ceil, kernel=None):
+    """One leg: per-kernel and per-call distributions, and the rate of the summed kernel time."""
+    ks = {n: dist(s) for n, s in per_kernel.items()}
+    mean_ms = sum(v["mean_ms"] for v in ks.values())
+    med_ms = sum(v["median_ms"] for v in ks.values())
+    rec = {"kernels": ks, "avg_ms": mean_ms, "call_device_ms": dist(per_call),
+           "wall_ms_per_call": wall / calls * 1e3, **rate_of(kind, amount, mean_ms, ceil),
+           "at_median": rate_of(kind, amount, med_ms, ceil)}
+    if kernel is not None:
+        rec["kernel"] = kernel
+    return rec
+
+
+def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
     """Extra legs: the 4k prefill forward (causal and not; bf16, then fp8 inputs), the 1k causal
     prefill, the step's forward+backward as one launch, the ragged prefill and its backward, GQA
-    decode over a contiguous and over a paged cache."""
+    decode over a contiguous and over a paged cache (each cold and warm)."""
     legs = {}
+
+    def timed(fn, between=None):
+        warm_up(torch, (lambda: (between(), fn())) if between else fn)
+        return time_calls(torch, lib, fn, calls, between)
+
     for name in ("prefill_4k_causal", "prefill_4k", "prefill_causal_1k"):
         w = I.WORKLOADS[name]
         t = {k: x.cuda() for k, x in I.make_prefill(w, with_dout=False).items()}
         o = torch.empty_like(t["q"])
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-        fn = lambda: lib.fwd(t["q"], t["k"], t["v"], w.causal, w.scale, out=o, lse=lse)  # noqa: E731
-        warm_up(torch, fn)
-        wall, stats = time_region(torch, lib, fn, reps)
-        (kname, st), = stats.items()
-        fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
-        legs[name] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": fl / (st["avg_ms"] * 1e-3) / 1e12,
-                      "frac_of_peak": fl / (st["avg_ms"] * 1e-3) / 1e12 / L.PEAK_BF16_TFLOPS,
-                      "wall_ms_per_call": wall / reps * 1e3}
-        log(f"[bench] leg {name}: {legs[name]['avg_ms']:.3f} ms, {legs[name]['tflops']:.1f} TFLOP/s")
+        wall, pk, pc = timed(lambda: lib.fwd(t["q"], t["k"], t["v"], w.causal, w.scale, out=o, lse=lse))
+        (kname,) = pk
+        legs[name] = leg_record(pk, pc, wall, calls, "mfma", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
+        log(f"[bench] leg {name}: {legs[name]['avg_ms']:.4f} ms (median {legs[name]['kernels'][kname]['median_ms']:.4f}),"
+            f" {legs[name]['tflops']:.1f} TFLOP/s")
         del t, o, lse
         torch.cuda.empty_cache()
 
@@ -285,15 +383,12 @@ def run_legs(torch, lib, I, L, reps=20):
         t = {k: x.cuda() for k, x in t8.items()}
         o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-        fn = lambda: lib.fwd_fp8(t["q"], t["k"], t["v"], ds, w.causal, w.scale, out=o, lse=lse)  # noqa: E731
-        warm_up(torch, fn)
-        wall, stats = time_region(torch, lib, fn, reps)
-        (kname, st), = stats.items()
-        fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal)
-        tf = fl / (st["avg_ms"] * 1e-3) / 1e12
-        legs[name] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": tf, "frac_of_peak": tf / L.PEAK_FP8_TFLOPS,
-                      "peak_tflops": L.PEAK_FP8_TFLOPS, "wall_ms_per_call": wall / reps * 1e3}
-        log(f"[bench] leg {name}: {st['avg_ms']:.3f} ms, {tf:.1f} TFLOP/s ({tf / L.PEAK_FP8_TFLOPS:.3f} of fp8 peak)")
+        wall, pk, pc = timed(lambda: lib.fwd_fp8(t["q"], t["k"], t["v"], ds, w.causal, w.scale, out=o, lse=lse))
+        (kname,) = pk
+        legs[name] = leg_record(pk, pc, wall, calls, "mfma8", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
+        legs[name]["peak_tflops"] = L.PEAK_FP8_TFLOPS
+        log(f"[bench] leg {name}: {legs[name]['avg_ms']:.4f} ms, {legs[name]['tflops']:.1f} TFLOP/s "
+            f"({legs[name]['frac_of_peak']:.3f} of fp8 peak)")
         del t, t8, o, lse
         torch.cuda.empty_cache()
 
@@ -304,15 +399,13 @@ def run_legs(torch, lib, I, L, reps=20):
                 dq=torch.empty(t["q"].shape, dtype=torch.float32, device="cuda"))
     outs["dk"], outs["dv"] = torch.empty_like(outs["dq"]), torch.empty_like(outs["dq"])
     wsf = torch.empty(lib.fwd_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
-    fn = lambda: lib.fwd_bwd(t["q"], t["k"], t["v"], t["do"], w.causal, w.scale, workspace=wsf, **outs)  # noqa
-    warm_up(torch, fn)
-    wall, stats = time_region(torch, lib, fn, reps)
-    (kname, st), = stats.items()
+    wall, pk, pc = timed(lambda: lib.fwd_bwd(t["q"], t["k"], t["v"], t["do"], w.causal, w.scale, workspace=wsf, **outs))
+    (kname,) = pk
     fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal) + L.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
-    tf = fl / (st["avg_ms"] * 1e-3) / 1e12
-    legs["fwdbwd_fused"] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": tf, "frac_of_peak": tf / L.PEAK_BF16_TFLOPS,
-                            "wall_ms_per_call": wall / reps * 1e3, "launches_per_call": 1}
-    log(f"[bench] leg fwdbwd_fused: {st['avg_ms']:.3f} ms, {tf:.1f} TFLOP/s (one launch)")
+    legs["fwdbwd_fused"] = leg_record(pk, pc, wall, calls, "mfma", fl, ceil, kname)
+    legs["fwdbwd_fused"]["launches_per_call"] = 1
+    log(f"[bench] leg fwdbwd_fused: {legs['fwdbwd_fused']['avg_ms']:.3f} ms, {legs['fwdbwd_fused']['tflops']:.1f} "
+        f"TFLOP/s (one launch)")
     del t, outs, wsf
     torch.cuda.empty_cache()
 
@@ -324,33 +417,26 @@ def run_legs(torch, lib, I, L, reps=20):
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.H, t["q"].shape[0]), dtype=torch.float32, device="cuda")
     max_len = int(lengths.max())
-    fn = lambda: lib.fwd_varlen(t["q"], t["k"], t["v"], cu, max_len, w.causal, w.scale, out=o, lse=lse)  # noqa
-    warm_up(torch, fn)
-    wall, stats = time_region(torch, lib, fn, reps)
-    (kname, st), = stats.items()
-    fl = L.varlen_fwd_flops(w.H, w.d, lengths, w.causal)
-    legs["prefill_varlen"] = {"kernel": kname, "avg_ms": st["avg_ms"], "tflops": fl / (st["avg_ms"] * 1e-3) / 1e12,
-                              "frac_of_peak": fl / (st["avg_ms"] * 1e-3) / 1e12 / L.PEAK_BF16_TFLOPS,
-                              "wall_ms_per_call": wall / reps * 1e3, "tokens": int(lengths.sum()),
-                              "sequences": int(len(lengths)), "max_len": max_len}
-    log(f"[bench] leg prefill_varlen: {st['avg_ms']:.3f} ms, {legs['prefill_varlen']['tflops']:.1f} TFLOP/s "
-        f"({int(lengths.sum())} tokens in {len(lengths)} sequences)")
+    wall, pk, pc = timed(lambda: lib.fwd_varlen(t["q"], t["k"], t["v"], cu, max_len, w.causal, w.scale, out=o,
+                                                lse=lse))
+    (kname,) = pk
+    legs["prefill_varlen"] = leg_record(pk, pc, wall, calls, "mfma", L.varlen_fwd_flops(w.H, w.d, lengths, w.causal),
+                                        ceil, kname)
+    legs["prefill_varlen"].update(tokens=int(lengths.sum()), sequences=int(len(lengths)), max_len=max_len)
+    log(f"[bench] leg prefill_varlen: {legs['prefill_varlen']['avg_ms']:.3f} ms, "
+        f"{legs['prefill_varlen']['tflops']:.1f} TFLOP/s ({int(lengths.sum())} tokens in {len(lengths)} sequences)")
 
     # The backward of the same ragged batch (attn_bwd_varlen: dQ kernel, then dK/dV kernel)
     f32 = dict(dtype=torch.float32, device="cuda")
     g = dict(dq=torch.empty(t["q"].shape, **f32), dk=torch.empty(t["k"].shape, **f32),
              dv=torch.empty(t["v"].shape, **f32))
     wsv = torch.empty(lib.bwd_varlen_workspace_size(t["q"].shape[0], w.H, w.d), dtype=torch.uint8, device="cuda")
-    fn = lambda: lib.bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, cu, max_len, w.causal, w.scale,  # noqa
-                                workspace=wsv, **g)
-    warm_up(torch, fn)
-    wall, stats = time_region(torch, lib, fn, reps)
-    ms = sum(st["avg_ms"] for st in stats.values())
+    wall, pk, pc = timed(lambda: lib.bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, cu, max_len, w.causal,
+                                                w.scale, workspace=wsv, **g))
     fl = sum(L.bwd_flops(1, w.H, int(n), w.d, w.causal) for n in lengths)
-    tf = fl / (ms * 1e-3) / 1e12
-    legs["prefill_varlen_bwd"] = {"kernels": {k: st["avg_ms"] for k, st in stats.items()}, "avg_ms": ms, "tflops": tf,
-                                  "frac_of_peak": tf / L.PEAK_BF16_TFLOPS, "wall_ms_per_call": wall / reps * 1e3}
-    log(f"[bench] leg prefill_varlen_bwd: {ms:.3f} ms, {tf:.1f} TFLOP/s (two kernels)")
+    legs["prefill_varlen_bwd"] = leg_record(pk, pc, wall, calls, "mfma", fl, ceil)
+    log(f"[bench] leg prefill_varlen_bwd: {legs['prefill_varlen_bwd']['avg_ms']:.3f} ms, "
+        f"{legs['prefill_varlen_bwd']['tflops']:.1f} TFLOP/s (two kernels)")
     del t, o, lse, cu, g, wsv
     torch.cuda.empty_cache()
 
@@ -358,52 +444,43 @@ def run_legs(torch, lib, I, L, reps=20):
     dense = I.make_decode(w)
     lens = dense["kv_len"].numpy().tolist()
     nbytes = L.decode_bytes(w.H, w.H_kv, w.d, 2, lens)
-    # Read (not written) before each call to evict the cache: a written buffer would leave dirty
+    # Read (not written) before each cold call to evict the cache: a written buffer would leave dirty
     # lines whose write-back then lands inside the timed kernel.
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB, above the 256 MB last-level cache
     o = torch.empty((w.B, w.H, w.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
-    wsd = torch.empty(lib.decode_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
+    wsd = torch.zeros(lib.decode_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
 
-    def cold_decode(fn, name, split_prefix, extra):
-        warm_up(torch, lambda: (flush.sum(), fn()))
-        # cold: the cache flush runs outside the timed kernels
-        lib.timing_reset()
-        lib.timing_enable(True)
-        for _ in range(reps):
-            lib.timing_enable(False)
-            flush.sum()
-            lib.timing_enable(True)
-            fn()
-        torch.cuda.synchronize()
-        lib.timing_enable(False)
-        stats = kernel_stats(lib)
-        lib.timing_reset()
-        total_ms = sum(s["avg_ms"] for s in stats.values())
-        split = [n for n in stats if n.startswith(split_prefix)][0]
-        legs[name] = {
-            "kernels": {n: s["avg_ms"] for n, s in stats.items()},
-            "compulsory_bytes": nbytes,
-            "gbs_split_kernel": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9,
-            "gbs_both_kernels": nbytes / (total_ms * 1e-3) / 1e9,
-            "frac_of_peak_split": nbytes / (stats[split]["avg_ms"] * 1e-3) / 1e9 / L.PEAK_HBM_GBS,
-            "cache": "cold (1 GiB buffer read before each call, outside the timed kernels)",
-            "tflops": L.decode_flops(w.H, w.d, lens) / (total_ms * 1e-3) / 1e12,
-            **extra,
-        }
-        log(f"[bench] leg {name}: {total_ms:.3f} ms, {legs[name]['gbs_both_kernels']:.0f} GB/s")
+    def decode_leg(fn, name, extra):
+        # cold (primary): every byte comes from HBM; warm: back-to-back calls, part of the 1.06 GB may
+        # still sit in the 256 MB last-level cache
+        wall, pk, pc = timed(fn, between=lambda: flush.sum())
+        rec = leg_record(pk, pc, wall, calls, "hbm", nbytes, ceil)
+        split = [n for n in pk if "split" in n][0]
+        rec.update(compulsory_bytes=nbytes, cache="cold (1 GiB buffer read before each call, outside the timed "
+                                                   "kernels and the call's events)",
+                   split_kernel=rate_of("hbm", nbytes, rec["kernels"][split]["mean_ms"], ceil),
+                   tflops=L.decode_flops(w.H, w.d, lens) / (rec["avg_ms"] * 1e-3) / 1e12, **extra)
+        wall_w, pk_w, pc_w = timed(fn)
+        warm = leg_record(pk_w, pc_w, wall_w, calls, "hbm", nbytes, ceil)
+        rec["warm"] = {"avg_ms": warm["avg_ms"], "gbs": warm["gbs"], "frac_of_peak": warm["frac_of_peak"],
+                       "kernels": warm["kernels"], "call_device_ms": warm["call_device_ms"]}
+        legs[name] = rec
+        log(f"[bench] leg {name}: {rec['avg_ms']:.4f} ms over {len(pk)} kernel(s), {rec['gbs']:.0f} GB/s "
+            f"({rec['frac_of_peak']:.3f} of 8 TB/s whole call; split kernel {rec['split_kernel']['gbs']:.0f} GB/s); "
+            f"warm {rec['warm']['gbs']:.0f} GB/s")
 
     t = {k: x.cuda() for k, x in dense.items()}
-    cold_decode(lambda: lib.decode(t["q"], t["k"], t["v"], t["kv_len"], w.scale, out=o, lse=lse, workspace=wsd),
-                "decode_gqa", "decode_split", {})
+    decode_leg(lambda: lib.decode(t["q"], t["k"], t["v"], t["kv_len"], w.scale, out=o, lse=lse, workspace=wsd),
+               "decode_gqa", {})
     del t
     paged = I.make_decode_paged(w, 64, dense=dense)
     del dense
     tp = {k: x.cuda() for k, x in paged.items()}
-    cold_decode(lambda: lib.decode_paged(tp["q"], tp["k_pages"], tp["v_pages"], tp["block_table"], tp["kv_len"],
-                                         w.scale, out=o, lse=lse, workspace=wsd),
-                "decode_gqa_paged", "decode_paged_split",
-                {"page_size": 64, "pages": int(paged["k_pages"].shape[0]), "placement": "seeded shuffle"})
+    decode_leg(lambda: lib.decode_paged(tp["q"], tp["k_pages"], tp["v_pages"], tp["block_table"], tp["kv_len"],
+                                        w.scale, out=o, lse=lse, workspace=wsd),
+               "decode_gqa_paged", {"page_size": 64, "pages": int(paged["k_pages"].shape[0]),
+                                    "placement": "seeded shuffle"})
     return legs
 
 

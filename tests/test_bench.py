@@ -44,3 +44,29 @@ def test_warm_up_runs_for_its_time_and_at_least_its_calls():
     calls.clear()
     n = bench.warm_up(FakeTorch, lambda: calls.append(1), seconds=0.05, min_calls=1)
     assert n == len(calls) >= 1
+
+
+def test_distribution_summary():
+    d = bench.dist([3.0, 1.0, 2.0, 4.0, 5.0])
+    assert d["n"] == 5 and d["median_ms"] == 3.0 and d["min_ms"] == 1.0 and d["max_ms"] == 5.0
+    assert d["p10_ms"] == 1.4 and abs(d["p90_ms"] - 4.6) < 1e-12 and d["mean_ms"] == 3.0
+    assert bench.dist([]) == {"n": 0}
+
+
+def test_host_record_names_the_cpus():
+    h = bench.host_record()
+    assert h["affinity_cpus"] >= 1 and h["cpu_model"]
+    assert h["numa_nodes"] is None or h["numa_nodes"] >= 1
+
+
+def test_rates_against_peak_and_ceiling():
+    ceil = {"mfma_bf16_tflops": 2000.0, "mfma_fp8_tflops": 4000.0, "hbm_read_gbs": 7000.0}
+    r = bench.rate_of("mfma", 2.5e12, 1.0, ceil)  # 2.5 TFLOP in 1 ms
+    assert abs(r["tflops"] - 2500.0) < 1e-9 and abs(r["frac_of_ceiling"] - 1.25) < 1e-12
+    r = bench.rate_of("hbm", 7e9, 1.0, ceil)  # 7 GB in 1 ms
+    assert abs(r["gbs"] - 7000.0) < 1e-9 and abs(r["frac_of_peak"] - 0.875) < 1e-12
+
+
+def test_committed_ceilings_without_measuring():
+    c = bench.ceilings(False)
+    assert c["mfma_bf16_tflops"] > 2000 and c["hbm_read_gbs"] > 6000 and "committed" in c["source"]
