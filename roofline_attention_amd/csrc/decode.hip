@@ -230,13 +230,13 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
     const float m_new = fmaxf(m_run, tmax);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
+    // The normaliser sums the bf16-rounded probabilities, the values that multiply V.
     bf16x8 pb;
     float tsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(x[e] - m_new);
-      tsum += p;
-      pb[e] = to_bf16(p);
+      pb[e] = to_bf16(fast_exp2(x[e] - m_new));
+      tsum += to_f32(pb[e]);
     }
     l_run = fmaf(l_run, alpha, tsum);
     // Unconditional rescale: a branch here would split the loop body, and the compiler would

@@ -70,7 +70,10 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 
 // Decode split size (keys per workgroup) and workspace layout: per (b, h, split) a record of
 // d + 4 floats {m, l, -, -, o[0..d)} (m in log2 units of the scaled score, o not yet divided by l).
-constexpr int kDecodeSplit = 1024;
+#ifndef RA_DECODE_SPLIT
+#define RA_DECODE_SPLIT 1024
+#endif
+constexpr int kDecodeSplit = RA_DECODE_SPLIT;
 size_t decode_workspace_bytes(int B, int H, int N_cap, int d);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* lse,
                          const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d,

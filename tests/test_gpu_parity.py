@@ -343,6 +343,42 @@ def test_decode_paged_full_workload_matches_dense(lib):
     assert torch.isfinite(o.float()).all()
 
 
+def test_decode_workspace_reuse_with_other_inputs(lib):
+    # One workspace serves calls on different inputs (contiguous and paged, one sequence of length
+    # 0, lengths on both sides of the 1024-key split): each call's records are written before the
+    # merge reads them, so no call sees another's partial results.
+    lens = [5000, 1, 1024, 1025, 3333, 0]
+    cases = []
+    for seed in (19, 20):
+        w = I.Workload("decws", "decode", 6, 16, 4, 5000, 128, "bf16", False, seed=seed, kv_lo=1, kv_hi=5000)
+        t = I.make_decode(w, nan_pad=False)
+        t["kv_len"] = torch.tensor(lens, dtype=torch.int32)
+        cases.append((w, t, {k: dev(x) for k, x in t.items()}))
+    w = cases[0][0]
+    ws = torch.full((lib.decode_workspace_size(w.B, w.H, w.N, w.d),), 0x7F, dtype=torch.uint8, device="cuda")
+    outs = {0: [], 1: []}
+    for rep in range(3):
+        for i, (w, t, g) in enumerate(cases):
+            o, lse = lib.decode(g["q"], g["k"], g["v"], g["kv_len"], w.scale, workspace=ws)
+            outs[i].append((o.cpu(), lse.cpu()))
+    for i, (w, t, g) in enumerate(cases):
+        o0, l0 = outs[i][0]
+        for o, lse in outs[i][1:]:
+            assert torch.equal(o, o0) and torch.equal(lse, l0)
+        tp = I.make_decode_paged(w, 128, dense=t)
+        op, lsep = lib.decode_paged(dev(tp["q"]), dev(tp["k_pages"]), dev(tp["v_pages"]), dev(tp["block_table"]),
+                                    dev(tp["kv_len"]), w.scale, workspace=ws)
+        assert torch.equal(op.cpu(), o0) and torch.equal(lsep.cpu(), l0)
+        q = f64(t["q"])
+        for b, n in enumerate(lens):
+            if n == 0:
+                assert torch.all(o0[b] == 0) and torch.all(torch.isneginf(l0[b]))
+                continue
+            ro, rl = orc.attention_decode(q[b:b + 1], f64(t["k"][b:b + 1, :, :n]), f64(t["v"][b:b + 1, :, :n]),
+                                          np.array([n]), w.scale)
+            assert max_err(o0[b:b + 1], ro) <= TOL_BF16 and max_err(l0[b:b + 1], rl) <= TOL_BF16
+
+
 def test_decode_zero_length_is_defined(lib):
     w = I.Workload("dec0", "decode", 2, 4, 4, 64, 128, "bf16", False, seed=17, kv_lo=1, kv_hi=64)
     t = I.make_decode(w)
@@ -544,5 +580,19 @@ def test_timer_reports_kernels(lib):
     finally:
         lib.timing_enable(False)
     rec = lib.timing_read()
+    smp = lib.timing_samples()
     lib.timing_reset()
     assert rec["fwd_bf16_d128_causal"][0] == 3 and rec["fwd_bf16_d128_causal"][1] > 0
+    # one duration per launch, summing to the total
+    per = smp["fwd_bf16_d128_causal"]
+    assert len(per) == 3 and all(x > 0 for x in per)
+    assert abs(sum(per) - rec["fwd_bf16_d128_causal"][1]) <= 1e-3 * rec["fwd_bf16_d128_causal"][1]
+    # releasing the events leaves the library usable: the timer creates new ones
+    lib.release()
+    lib.timing_enable(True)
+    try:
+        lib.fwd(dev(t["q"]), dev(t["k"]), dev(t["v"]), True, w.scale)
+    finally:
+        lib.timing_enable(False)
+    assert lib.timing_read()["fwd_bf16_d128_causal"][0] == 1
+    lib.release()
