@@ -135,6 +135,24 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode with no allocation and no workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same operation, arguments (less the workspace) and results as attn_decode, bit for bit: the
+ * split records live in a fixed scratch array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends. The call makes no hipMalloc, hipFree or other
+ * allocating call (with the opt-in timer below off: its events are its only objects); the first
+ * call on a device looks up the array's address there (hipGetSymbolAddress) and caches it.
+ * Shapes whose attn_decode_workspace_size(B, H, N_cap, d) exceeds the scratch are rejected with
+ * ATTN_ERR_WORKSPACE before any device work. Every call on one GPU shares that GPU's scratch, so
+ * calls that overlap in time on one GPU (other streams, other host threads) race and give wrong
+ * results; calls ordered on one stream are safe. The scratch needs no initial contents.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, int causal,
+                                float scale, int dtype, void* stream);
+
+/*
  * Decode over a paged KV cache: as attn_decode, but the cache lives in fixed-size pages that need
  * not be contiguous or in order. A kernel's contract has to state the page layout when K/V is not
  * contiguous ("M4.2 - GPU Execution Model for Transformer Kernels", section 0x06), and logical

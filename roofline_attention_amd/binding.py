@@ -38,6 +38,7 @@ SIGNATURES = {
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_decode_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
+    "attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
@@ -236,6 +237,32 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len
     _check(_lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(kv_len), B, H, H_kv,
                             N_cap, d, 0, float(scale), ATTN_BF16, _ptr(workspace), workspace.numel(),
                             _stream(q.device)))
+    return out, lse
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len: torch.Tensor,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None):
+    """decode() on the library's fixed scratch (attn_decode_noalloc): no workspace, no allocation in
+    the library. Outputs the caller does not pass are allocated here by torch. Returns (o, lse)."""
+    _need(q, "q", torch.bfloat16)
+    B, H, d = q.shape
+    H_kv, N_cap = k_cache.shape[1], k_cache.shape[2]
+    _need(k_cache, "k_cache", torch.bfloat16, (B, H_kv, N_cap, d), q.device)
+    _need(v_cache, "v_cache", torch.bfloat16, (B, H_kv, N_cap, d), q.device)
+    _need(kv_len, "kv_len", torch.int32, (B,), q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape, q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, H), q.device)
+    _check(_lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(kv_len), B, H,
+                                    H_kv, N_cap, d, 0, float(scale), ATTN_BF16, _stream(q.device)))
     return out, lse
 
 

@@ -230,10 +230,16 @@ size_t attn_decode_workspace_size(int B, int H, int N_cap, int d) {
   return ra::decode_workspace_bytes(B, H, N_cap, d);
 }
 
-attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                        const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, int causal, float scale,
-                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)causal;
+}  // extern "C"
+
+namespace {
+
+// Checks of a contiguous decode call shared by attn_decode and attn_decode_noalloc; `workspace`
+// (need bytes) is the caller's buffer, or nullptr for the library's fixed scratch, which cannot
+// overlap caller memory.
+attn_status check_decode(const void* q, const void* k_cache, const void* v_cache, const void* o, const float* lse,
+                         const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, float scale, int dtype,
+                         const void* workspace, size_t need) {
   if (!q || !k_cache || !v_cache || !o || !kv_len)
     return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache, o and kv_len must be non-null");
   attn_status st = check_shape(B, H, H_kv, N_cap, d, scale);
@@ -247,12 +253,9 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(kv_len) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return fail(ATTN_ERR_INVALID_ARG, "kv_len and lse must be 4-byte aligned");
-  const size_t need = ra::decode_workspace_bytes(B, H, N_cap, d);
-  if (workspace == nullptr || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "decode workspace too small");
-  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const size_t qb = (size_t)B * H * d * 2, cb = (size_t)B * H_kv * N_cap * d * 2;
   const Range rq{q, qb}, rk{k_cache, cb}, rv{v_cache, cb}, ro{o, qb}, rl{lse, lse ? (size_t)B * H * 4 : 0},
-      rw{workspace, need}, rn{kv_len, (size_t)B * 4};
+      rw{workspace, workspace ? need : 0}, rn{kv_len, (size_t)B * 4};
   const Range outs[] = {ro, rl, rw};
   const Range ins[] = {rq, rk, rv, rn};
   for (const Range& a : outs)
@@ -260,7 +263,43 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
       if (overlap(a, b)) return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap inputs");
   if (overlap(ro, rl) || overlap(ro, rw) || overlap(rl, rw))
     return fail(ATTN_ERR_INVALID_ARG, "outputs or workspace overlap each other");
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, int causal, float scale,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)causal;
+  attn_status st = check_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, dtype, nullptr, 0);
+  if (st != ATTN_OK) return st;
+  const size_t need = ra::decode_workspace_bytes(B, H, N_cap, d);
+  if (workspace == nullptr || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "decode workspace too small");
+  if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  st = check_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, dtype, workspace, need);
+  if (st != ATTN_OK) return st;
   return hip_status(ra::launch_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d, int causal,
+                                float scale, int dtype, void* stream) {
+  (void)causal;
+  attn_status st = check_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, dtype, nullptr, 0);
+  if (st != ATTN_OK) return st;
+  const size_t need = ra::decode_workspace_bytes(B, H, N_cap, d);
+  if (need > ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTN_ERR_WORKSPACE,
+                "attn_decode_noalloc: B * H * ceil(N_cap / 1024) * (d + 4) * 4 bytes of split records exceed the "
+                "library's fixed scratch (ATTN_DECODE_NOALLOC_SCRATCH_BYTES); use attn_decode with a workspace");
+  void* scratch = nullptr;
+  const hipError_t e = ra::decode_scratch_address(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(ra::launch_decode(q, k_cache, v_cache, o, lse, kv_len, B, H, H_kv, N_cap, d, scale, scratch,
                                       static_cast<hipStream_t>(stream)));
 }
 

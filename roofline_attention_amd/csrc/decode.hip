@@ -18,12 +18,24 @@
 //   O = sum 2^(m_s - M) o_s / L, LSE = ln 2 * (M + log2 L).
 #include <math.h>
 
+#include <atomic>
+
+#include "../../include/attn.h"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "lds_tile.hpp"
 
 namespace ra {
 namespace {
+
+// Split-record scratch of attn_decode_noalloc, for callers that cannot allocate: one copy per GPU
+// the library runs on, held until the process ends. In host code this name is only a stand-in for
+// the symbol; kernels receive the device address that hipGetSymbolAddress returns
+// (decode_scratch_address below), never the name itself. The records need no initial contents.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // per device: scratch's device address, once known
 
 
 constexpr int DEC_WAVES = 4;                             // waves per workgroup
@@ -458,6 +470,23 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
   const Pages none{nullptr, 1, 0, 1};
   return d == 128 ? launch_g<128, false>(G, q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream, none)
                   : launch_g<64, false>(G, q, kc, vc, o, lse, kv_len, B, H, H_kv, N_cap, scale, ws, stream, none);
+}
+
+hipError_t decode_scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  void* p = cached ? g_scratch_ptr[dev].load(std::memory_order_acquire) : nullptr;
+  if (p == nullptr) {
+    // with the device current: each GPU holds its own copy of the array at its own address
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    if (cached) g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,

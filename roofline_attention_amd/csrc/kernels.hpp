@@ -78,6 +78,9 @@ size_t decode_workspace_bytes(int B, int H, int N_cap, int d);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* lse,
                          const int32_t* kv_len, int B, int H, int H_kv, int N_cap, int d,
                          float scale, void* ws, hipStream_t stream);
+// Device address of the library's fixed decode scratch (ATTN_DECODE_NOALLOC_SCRATCH_BYTES) on the
+// current device, looked up once per device and cached.
+hipError_t decode_scratch_address(void** ptr);
 
 // Paged caches: k_pages, v_pages [num_pages, H_kv, page_size, d], block_table [B, max_pages] of
 // physical page ids; page_size a power of two in [32, 1024]. Same workspace as launch_decode with

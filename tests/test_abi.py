@@ -179,6 +179,26 @@ def test_decode_validation(lib):
     assert lib.attn_decode_workspace_size(1, 1, 1, 96) == 0
 
 
+def test_decode_noalloc_validation(lib):
+    # rejected before any HIP call: bad arguments as for attn_decode, and shapes whose split records
+    # exceed the library's fixed 16 MiB scratch
+    p = [addr(i) for i in range(6)]
+
+    def call(B=64, H=32, H_kv=8, N_cap=8192, d=128, dtype=BF16, ptrs=None):
+        q = ptrs if ptrs is not None else p
+        return lib.attn_decode_noalloc(*q, B, H, H_kv, N_cap, d, 0, 0.088, dtype, None)
+
+    assert call(N_cap=16384) == WORKSPACE  # 64 x 32 x 16 splits x 528 B = 17.3 MB
+    assert b"scratch" in lib.attn_last_error()
+    assert call(d=96) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(H=30) == INVALID
+    assert call(ptrs=p[:5] + [None]) == INVALID  # kv_len is required
+    ov = list(p)
+    ov[3] = p[0]  # o on top of q
+    assert call(ptrs=ov) == INVALID
+
+
 def test_decode_paged_validation(lib):
     p = [addr(i) for i in range(8)]
     ws_need = lib.attn_decode_workspace_size(64, 32, 128 * 64, 128)
