@@ -83,6 +83,12 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// sum over the same lane pair (one VALU exchange; no lane-index address as for a shuffle)
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 
 // One work item of the forward: query tile `item` of the grid's ordering (a pair of tiles under a
 // causal mask). The standalone kernel's item (FUSED false) declares its LDS tiles here; inside the
@@ -170,10 +176,13 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
     const float c = fmaxf(neg ? -scale_log2 : scale_log2, FLT_MIN);
     bf16x8 qf[KSTEPS];
     if (qi < Nb) {
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + q_base + (size_t)qi * rs_q);
+      // row address from the lane index, as in the epilogue: a causal workgroup's second tile then
+      // needs no pointer kept from the first
+      const int lane_q = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + q_base + (size_t)(q0 + (lane_q & 31)) * rs_q);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        qf[kk] = src[2 * kk + g];
+        qf[kk] = src[2 * kk + (lane_q >> 5)];
         if (neg) qf[kk] = -qf[kk];
       }
     } else {
@@ -201,15 +210,19 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       const int row0 = kt * FWD_BC;
       const u32x4 rsrc = dma_rsrc(k_head + (size_t)row0 * rs_kv, tile_bytes(row0));
 #pragma unroll
-      for (int u = 0; u < BLOCKS / FWD_WAVES; ++u)
-        load_to_lds<16>(rsrc, k_voff + u * BLK_BYTES, &sm.k[stage][(u * FWD_WAVES + w) * RPI * HD]);
+      for (int u = 0; u < BLOCKS / FWD_WAVES; ++u) {
+        if (u == 0) load_to_lds<16>(rsrc, k_voff, &sm.k[stage][w * RPI * HD]);
+        else load_to_lds16_so(rsrc, k_voff, u * BLK_BYTES, &sm.k[stage][(u * FWD_WAVES + w) * RPI * HD]);
+      }
     };
     auto issue_v = [&](int kt, int stage) {
       const int row0 = kt * FWD_BC;
       const u32x4 rsrc = dma_rsrc(v_head + (size_t)row0 * rs_kv, tile_bytes(row0));
 #pragma unroll
-      for (int u = 0; u < BLOCKS / FWD_WAVES; ++u)
-        load_to_lds<16>(rsrc, v_voff + u * BLK_BYTES, &sm.v[stage][(u * FWD_WAVES + w) * RPI * HD]);
+      for (int u = 0; u < BLOCKS / FWD_WAVES; ++u) {
+        if (u == 0) load_to_lds<16>(rsrc, v_voff, &sm.v[stage][w * RPI * HD]);
+        else load_to_lds16_so(rsrc, v_voff, u * BLK_BYTES, &sm.v[stage][(u * FWD_WAVES + w) * RPI * HD]);
+      }
     };
 
     // K A-operand read (S^T block kb, k-step kk): row 32kb + l32, chunk 2kk + g at position
@@ -395,17 +408,25 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       step(kt, s_cur, s_alt);
       step(kt + 1, s_alt, s_cur);
     }
+    // One last() on one buffer: inlining it on either buffer made the compiler merge the two copies
+    // with register shuffles and spill around the rescale branch.
     if (kt + 1 < n_kt) {
       step(kt, s_cur, s_alt);
-      last(kt + 1, s_alt);
-    } else {
-      last(kt, s_cur);
+      s_cur[0] = s_alt[0];
+      s_cur[1] = s_alt[1];
+      ++kt;
     }
+    last(kt, s_cur);
 
-    l_run += __shfl_xor(l_run, 32, 64);
-    if (qi < Nb) {
+    l_run = pair_sum(l_run);
+    // The epilogue takes its row from the lane index (v_mbcnt) instead of the prologue's
+    // registers, so no per-lane address has to stay live across the tile loop for it.
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int qi_e = q0 + (lane_e & 31);
+    const int g_e = lane_e >> 5;
+    if (qi_e < Nb) {
       const float inv = 1.f / l_run;
-      bf16* orow = O + q_base + (size_t)qi * rs_q;
+      bf16* orow = O + q_base + (size_t)qi_e * rs_q;
       float dsum = 0.f;  // this lane's half of D_i (FUSED)
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) {
@@ -413,9 +434,10 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
         for (int rg = 0; rg < 4; ++rg) {
           bf16x4 t = {to_bf16(oacc[cb][4 * rg + 0] * inv), to_bf16(oacc[cb][4 * rg + 1] * inv),
                       to_bf16(oacc[cb][4 * rg + 2] * inv), to_bf16(oacc[cb][4 * rg + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * rg + 4 * g) = t;
+          *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * rg + 4 * g_e) = t;
           if constexpr (FUSED) {
-            const bf16x4 d4 = *reinterpret_cast<const bf16x4*>(dO + q_base + (size_t)qi * rs_q + 32 * cb + 8 * rg + 4 * g);
+            const bf16x4 d4 =
+                *reinterpret_cast<const bf16x4*>(dO + q_base + (size_t)qi_e * rs_q + 32 * cb + 8 * rg + 4 * g_e);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dsum = fmaf(to_f32(t[e]), to_f32(d4[e]), dsum);
           }
@@ -423,14 +445,14 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       }
       if constexpr (FUSED) {
         const float lse_row = (m_run + log2f(l_run)) * kLn2;
-        dsum += __shfl_xor(dsum, 32, 64);  // lanes l and l ^ 32 hold the two column halves of row qi
-        if (g == 0) {
-          LSE[lse_base + qi] = lse_row;
-          Dg[lse_base + qi] = dsum;
-          L2[lse_base + qi] = lse_row * kLog2e;
+        dsum = pair_sum(dsum);  // lanes l and l ^ 32 hold the two column halves of row qi
+        if (g_e == 0) {
+          LSE[lse_base + qi_e] = lse_row;
+          Dg[lse_base + qi_e] = dsum;
+          L2[lse_base + qi_e] = lse_row * kLog2e;
         }
       } else {
-        if (LSE != nullptr && g == 0) LSE[lse_base + qi] = (m_run + log2f(l_run)) * kLn2;
+        if (LSE != nullptr && g_e == 0) LSE[lse_base + qi_e] = (m_run + log2f(l_run)) * kLn2;
       }
     }
   }

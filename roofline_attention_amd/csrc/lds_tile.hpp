@@ -72,6 +72,16 @@ __device__ __forceinline__ void load_to_lds(const u32x4& rsrc, int voffset, cons
     asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0) : "memory");
 }
 
+// The same 16-byte load with a wave-uniform byte offset `soffset` added in the instruction's scalar
+// offset operand: a wave's blocks that sit a fixed (uniform) distance apart share one per-lane
+// voffset register instead of one each.
+__device__ __forceinline__ void load_to_lds16_so(const u32x4& rsrc, int voffset, int soffset, const void* lds_block) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_block;
+  asm volatile("buffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0),
+               "s"(__builtin_amdgcn_readfirstlane(soffset))
+               : "memory");
+}
+
 // Transposing read: in each 16-lane group, lane 4e + j supplies the address of 4 bf16 at row e
 // of a 4-row block; lane i of the group receives the 4 elements of column i of that block.
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
