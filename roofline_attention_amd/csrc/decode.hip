@@ -336,6 +336,8 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+constexpr int kFastSplits = 8;  // split counts the combine merges with one round of loads
+
 // One wave per (query head, sequence). Lane s holds (m, l) of split s (64 splits per pass), so
 // M, the weights 2^(m_s - M) and L take one round of parallel loads and wave reductions; the
 // output then sums the splits' partial rows with independent loads, PER elements per lane.
@@ -349,16 +351,62 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
+  bf16* out = Od + ((size_t)b * H + h) * HD;
+  const float* recs = ws + ((size_t)b * H + h) * n_split * REC;
+  if (n_split <= kFastSplits) {
+    // Up to kFastSplits splits (caches of up to 8192 rows): every record load is issued at once,
+    // beside the length load, so the merge costs one memory round trip instead of three (length,
+    // then maxima, then partial rows). Records of splits at or past the sequence's last one lie
+    // inside the workspace but were not written by this call; selects, not zero weights, keep them
+    // out (they may hold anything, NaN included).
+    float2 ml = make_float2(-INFINITY, 0.f);
+    if (lane < n_split) ml = *reinterpret_cast<const float2*>(recs + (size_t)lane * REC);
+    float v[kFastSplits][PER];
+#pragma unroll
+    for (int j = 0; j < kFastSplits; ++j) {
+      if (j < n_split) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[j][e] = recs[(size_t)j * REC + 4 + lane * PER + e];
+      }
+    }
+    const int len = clamp_len(kv_len, b, N_cap);
+    const int ns = (len + kDecodeSplit - 1) / kDecodeSplit;
+    if (ns == 0) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bf16(0.f);
+      if (lse != nullptr && lane == 0) lse[(size_t)b * H + h] = -INFINITY;
+      return;
+    }
+    const bool mine = lane < ns;
+    const float m = mine ? ml.x : -INFINITY;
+    const float M = wave_max(m);  // finite: every split below ns holds at least one key
+    const float wgt = mine ? fast_exp2(m - M) : 0.f;
+    const float L = wave_sum(mine ? wgt * ml.y : 0.f);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kFastSplits; ++j) {
+      if (j < ns) {  // uniform over the wave
+        const float wj = __shfl(wgt, j, 64);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, v[j][e], acc[e]);
+      }
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bf16(acc[e] * inv);
+    if (lse != nullptr && lane == 0) lse[(size_t)b * H + h] = (M + log2f(L)) * kLn2;
+    return;
+  }
   const int len = clamp_len(kv_len, b, N_cap);
   const int ns = (len + kDecodeSplit - 1) / kDecodeSplit;
-  bf16* out = Od + ((size_t)b * H + h) * HD;
   if (ns == 0) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) out[lane * PER + e] = to_bf16(0.f);
     if (lse != nullptr && lane == 0) lse[(size_t)b * H + h] = -INFINITY;
     return;
   }
-  const float* recs = ws + ((size_t)b * H + h) * n_split * REC;
   auto ml_of = [&](int s) {
     return s < ns ? *reinterpret_cast<const float2*>(recs + (size_t)s * REC) : make_float2(-INFINITY, 0.f);
   };
