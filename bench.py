@@ -3,13 +3,15 @@
 A step is one forward + backward pass (attn_fwd then attn_bwd, all forward and backward kernels)
 of causal bf16 attention over the [B=2, H=16, N=4096, d=128] synthetic batch, inputs resident in
 HBM before timing starts. The decode kernels and the prefill forwards are timed as extra legs in
-the same run and reported beside the step. Kernel durations come from HIP events that the library
-records on its launch stream around every kernel while its timer is enabled; every timed call
-keeps its own sample, so each figure carries its median, p10, p90 and minimum ("M4.2 - GPU
-Execution Model for Transformer Kernels", section 0x0B, Level 4: report a median and a tail, not
-one timing). Rates are priced against the published MI355X peaks and against ceilings measured on
-the same GPU in the same run ("Why Fast GPUs Still Wait for Memory", section "pi is the top of a
-stack": measure your own ceilings before trusting them).
+the same run and reported beside the step. Every timed region runs three passes of its calls: back
+to back with events only at the loop's two ends (the throughput figure), with an event pair on the
+launch stream around each call (the per-call distribution: median, p10, p90, minimum), and with the
+library's timer on, whose events around every kernel give each kernel's launch durations ("M4.2 -
+GPU Execution Model for Transformer Kernels", section 0x0B, Level 4: report a median and a tail,
+not one timing). The launch-bound 1k prefill is also replayed from a HIP graph of its calls, for
+comparison (a graph takes the host's launch cost out). Rates are priced against the published MI355X peaks
+and against ceilings measured on the same GPU in the same run ("Why Fast GPUs Still Wait for
+Memory", section "pi is the top of a stack": measure your own ceilings before trusting them).
 
 Output: one JSON line on stdout (rank 0), with the roofline of the dominant kernel and the fp64
 CPU oracle timed on a bounded sample of the same workload.
@@ -32,7 +34,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd/bwd TFLOP/s and decode HBM GB/s, % of MI355X roofline"
 WARMUP_S = 0.2  # untimed seconds of load before every timed region (the clock ramps up first)
-LEG_CALLS = 30  # timed calls per leg (>= 20 samples each)
+LEG_CALLS = 30  # timed calls per leg and pass (>= 20 samples each)
+GRAPH_REPLAYS = 20  # timed replays of a graph of LEG_CALLS calls (launch-bound legs)
 
 # Ceilings measured by the ceiling microbenchmarks (csrc/ceilings.hip) on one MI355X, used only when
 # the executable is not available in this run: dense bf16 and E4M3 MFMA on the full chip after a
@@ -135,30 +138,78 @@ def warm_up(torch, fn, seconds=WARMUP_S, min_calls=3):
 
 
 def time_calls(torch, lib, fn, calls, between=None):
-    """Runs fn() `calls` times back to back between two synchronisations, with the library's timer
-    on. Returns (wall seconds, {kernel: per-launch ms}, per-call ms). A call's duration is the time
-    between events recorded on the launch stream before and after it; `between`, if given, runs
-    before each call outside the timer and outside the call's events (e.g. a cache flush)."""
-    lib.timing_reset()
-    torch.cuda.synchronize()
+    """Three passes of `calls` calls of fn(), each ended by a synchronisation:
+    1. back to back with the library timer off and no event between calls (skipped when `between`
+       is given): host wall time and the device time between events at the loop's two ends;
+    2. an event pair on the launch stream around each call, timer off: the per-call distribution
+       (these events sit at call boundaries only, so a call's kernels run as they would untimed);
+    3. the library timer on: every launch's duration from events recorded around it.
+    `between`, if given, runs before each call outside the timer and outside the call's events (e.g.
+    a cache flush). Returns a dict: wall_s and loop_ms (pass 1, or None), per_call (ms, pass 2),
+    per_kernel ({kernel: [ms]}, pass 3)."""
+    res = {"wall_s": None, "loop_ms": None}
+    lib.timing_enable(False)
+    if between is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res["wall_s"] = time.perf_counter() - t0
+        res["loop_ms"] = e0.elapsed_time(e1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        if between is not None:
+            between()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    res["per_call"] = [a.elapsed_time(b) for a, b in ev]
+    lib.timing_reset()
     lib.timing_enable(True)
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
+    for _ in range(calls):
         if between is not None:
             lib.timing_enable(False)
             between()
             lib.timing_enable(True)
-        e0.record()
         fn()
-        e1.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     lib.timing_enable(False)
-    per_kernel = lib.timing_samples()
+    res["per_kernel"] = lib.timing_samples()
     lib.timing_reset()
-    per_call = [e0.elapsed_time(e1) for e0, e1 in ev]
-    return t1 - t0, per_kernel, per_call
+    return res
+
+
+def time_graph(torch, fn, calls, replays=GRAPH_REPLAYS):
+    """fn() captured `calls` times into one HIP graph (the library only enqueues kernels on the
+    current stream), replayed `replays` times with an event pair around each replay: per-call device
+    time without host launch cost, for launch-bound shapes. Returns per-replay ms / calls."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for a, b in ev:
+        a.record()
+        graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    out = [a.elapsed_time(b) / calls for a, b in ev]
+    del graph
+    return out
 
 
 def host_record():
@@ -265,7 +316,8 @@ def main():
     n_warm = warm_up(torch, step, seconds=WARMUP_S, min_calls=a.warmup)
     warm_s = time.perf_counter() - t_w
     log(f"[bench] warm-up {n_warm} steps in {warm_s:.2f} s; timing {a.steps} steps")
-    wall, per_kernel, per_step = time_calls(torch, lib, step, a.steps)
+    tm = time_calls(torch, lib, step, a.steps)
+    wall, per_kernel, per_step = tm["wall_s"], tm["per_kernel"], tm["per_call"]
     ms_per_step = wall / a.steps * 1e3
     step_flops = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal) + L.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
     value = step_flops / (wall / a.steps) / 1e12
@@ -320,6 +372,7 @@ def main():
         "warmup_calls": n_warm,
         "warmup_s": warm_s,
         "ms_per_step": ms_per_step,
+        "loop_device_ms_per_step": tm["loop_ms"] / a.steps,
         "step_device_ms": dist(per_step),
         "step_samples_ms": [round(x, 5) for x in per_step],
         "higher_is_better": True,
@@ -339,14 +392,24 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def leg_record(per_kernel, per_call, wall, calls, kind, amount, ceil, kernel=None):
-    """One leg: per-kernel and per-call distributions, and the rate of the summed kernel time."""
-    ks = {n: dist(s) for n, s in per_kernel.items()}
-    mean_ms = sum(v["mean_ms"] for v in ks.values())
-    med_ms = sum(v["median_ms"] for v in ks.values())
-    rec = {"kernels": ks, "avg_ms": mean_ms, "call_device_ms": dist(per_call),
-           "wall_ms_per_call": wall / calls * 1e3, **rate_of(kind, amount, mean_ms, ceil),
-           "at_median": rate_of(kind, amount, med_ms, ceil)}
+def leg_record(tm, calls, kind, amount, ceil, kernel=None):
+    """One leg from time_calls' passes. The leg's time per call (avg_ms, and the rates) is the device
+    time of the back-to-back loop divided by the calls (pass 1), or, for legs with work between
+    calls, the mean of the per-call event pairs (pass 2). `kernels` holds each kernel's launch
+    durations from the library timer (pass 3), whose events around every launch add a few
+    microseconds to each."""
+    ks = {n: dist(s) for n, s in tm["per_kernel"].items()}
+    pc = dist(tm["per_call"])
+    if tm["loop_ms"] is not None:
+        mean_ms, med_ms, source = tm["loop_ms"] / calls, pc["median_ms"], "back-to-back loop"
+    else:
+        mean_ms, med_ms, source = pc["mean_ms"], pc["median_ms"], "per-call events"
+    rec = {"avg_ms": mean_ms, "time_source": source, **rate_of(kind, amount, mean_ms, ceil),
+           "at_median": rate_of(kind, amount, med_ms, ceil), "call_device_ms": pc, "kernels": ks,
+           "kernels_sum_ms": sum(v["mean_ms"] for v in ks.values())}
+    if tm["loop_ms"] is not None:
+        rec["loop_ms_per_call"] = tm["loop_ms"] / calls
+        rec["wall_ms_per_call"] = tm["wall_s"] / calls * 1e3
     if kernel is not None:
         rec["kernel"] = kernel
     return rec
@@ -367,11 +430,18 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
         t = {k: x.cuda() for k, x in I.make_prefill(w, with_dout=False).items()}
         o = torch.empty_like(t["q"])
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-        wall, pk, pc = timed(lambda: lib.fwd(t["q"], t["k"], t["v"], w.causal, w.scale, out=o, lse=lse))
-        (kname,) = pk
-        legs[name] = leg_record(pk, pc, wall, calls, "mfma", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
-        log(f"[bench] leg {name}: {legs[name]['avg_ms']:.4f} ms (median {legs[name]['kernels'][kname]['median_ms']:.4f}),"
-            f" {legs[name]['tflops']:.1f} TFLOP/s")
+        def call():
+            lib.fwd(t["q"], t["k"], t["v"], w.causal, w.scale, out=o, lse=lse)
+        tm = timed(call)
+        (kname,) = tm["per_kernel"]
+        legs[name] = leg_record(tm, calls, "mfma", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
+        if name == "prefill_causal_1k":
+            # a launch-bound call: the same calls replayed from a HIP graph, for comparison
+            g = dist(time_graph(torch, call, calls))
+            legs[name]["graph_replay"] = {"ms_per_call": g, **rate_of("mfma", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal),
+                                                                       g["mean_ms"], ceil)}
+        log(f"[bench] leg {name}: {legs[name]['avg_ms']:.4f} ms ({legs[name]['time_source']}), "
+            f"{legs[name]['tflops']:.1f} TFLOP/s")
         del t, o, lse
         torch.cuda.empty_cache()
 
@@ -383,9 +453,9 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
         t = {k: x.cuda() for k, x in t8.items()}
         o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-        wall, pk, pc = timed(lambda: lib.fwd_fp8(t["q"], t["k"], t["v"], ds, w.causal, w.scale, out=o, lse=lse))
-        (kname,) = pk
-        legs[name] = leg_record(pk, pc, wall, calls, "mfma8", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
+        tm = timed(lambda: lib.fwd_fp8(t["q"], t["k"], t["v"], ds, w.causal, w.scale, out=o, lse=lse))
+        (kname,) = tm["per_kernel"]
+        legs[name] = leg_record(tm, calls, "mfma8", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
         legs[name]["peak_tflops"] = L.PEAK_FP8_TFLOPS
         log(f"[bench] leg {name}: {legs[name]['avg_ms']:.4f} ms, {legs[name]['tflops']:.1f} TFLOP/s "
             f"({legs[name]['frac_of_peak']:.3f} of fp8 peak)")
@@ -399,10 +469,10 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
                 dq=torch.empty(t["q"].shape, dtype=torch.float32, device="cuda"))
     outs["dk"], outs["dv"] = torch.empty_like(outs["dq"]), torch.empty_like(outs["dq"])
     wsf = torch.empty(lib.fwd_bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda")
-    wall, pk, pc = timed(lambda: lib.fwd_bwd(t["q"], t["k"], t["v"], t["do"], w.causal, w.scale, workspace=wsf, **outs))
-    (kname,) = pk
+    tm = timed(lambda: lib.fwd_bwd(t["q"], t["k"], t["v"], t["do"], w.causal, w.scale, workspace=wsf, **outs))
+    (kname,) = tm["per_kernel"]
     fl = L.fwd_flops(w.B, w.H, w.N, w.d, w.causal) + L.bwd_flops(w.B, w.H, w.N, w.d, w.causal)
-    legs["fwdbwd_fused"] = leg_record(pk, pc, wall, calls, "mfma", fl, ceil, kname)
+    legs["fwdbwd_fused"] = leg_record(tm, calls, "mfma", fl, ceil, kname)
     legs["fwdbwd_fused"]["launches_per_call"] = 1
     log(f"[bench] leg fwdbwd_fused: {legs['fwdbwd_fused']['avg_ms']:.3f} ms, {legs['fwdbwd_fused']['tflops']:.1f} "
         f"TFLOP/s (one launch)")
@@ -417,11 +487,10 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.H, t["q"].shape[0]), dtype=torch.float32, device="cuda")
     max_len = int(lengths.max())
-    wall, pk, pc = timed(lambda: lib.fwd_varlen(t["q"], t["k"], t["v"], cu, max_len, w.causal, w.scale, out=o,
-                                                lse=lse))
-    (kname,) = pk
-    legs["prefill_varlen"] = leg_record(pk, pc, wall, calls, "mfma", L.varlen_fwd_flops(w.H, w.d, lengths, w.causal),
-                                        ceil, kname)
+    tm = timed(lambda: lib.fwd_varlen(t["q"], t["k"], t["v"], cu, max_len, w.causal, w.scale, out=o, lse=lse))
+    (kname,) = tm["per_kernel"]
+    legs["prefill_varlen"] = leg_record(tm, calls, "mfma", L.varlen_fwd_flops(w.H, w.d, lengths, w.causal), ceil,
+                                        kname)
     legs["prefill_varlen"].update(tokens=int(lengths.sum()), sequences=int(len(lengths)), max_len=max_len)
     log(f"[bench] leg prefill_varlen: {legs['prefill_varlen']['avg_ms']:.3f} ms, "
         f"{legs['prefill_varlen']['tflops']:.1f} TFLOP/s ({int(lengths.sum())} tokens in {len(lengths)} sequences)")
@@ -431,10 +500,10 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
     g = dict(dq=torch.empty(t["q"].shape, **f32), dk=torch.empty(t["k"].shape, **f32),
              dv=torch.empty(t["v"].shape, **f32))
     wsv = torch.empty(lib.bwd_varlen_workspace_size(t["q"].shape[0], w.H, w.d), dtype=torch.uint8, device="cuda")
-    wall, pk, pc = timed(lambda: lib.bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, cu, max_len, w.causal,
-                                                w.scale, workspace=wsv, **g))
+    tm = timed(lambda: lib.bwd_varlen(t["q"], t["k"], t["v"], o, t["do"], lse, cu, max_len, w.causal, w.scale,
+                                      workspace=wsv, **g))
     fl = sum(L.bwd_flops(1, w.H, int(n), w.d, w.causal) for n in lengths)
-    legs["prefill_varlen_bwd"] = leg_record(pk, pc, wall, calls, "mfma", fl, ceil)
+    legs["prefill_varlen_bwd"] = leg_record(tm, calls, "mfma", fl, ceil)
     log(f"[bench] leg prefill_varlen_bwd: {legs['prefill_varlen_bwd']['avg_ms']:.3f} ms, "
         f"{legs['prefill_varlen_bwd']['tflops']:.1f} TFLOP/s (two kernels)")
     del t, o, lse, cu, g, wsv
@@ -454,19 +523,18 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
     def decode_leg(fn, name, extra):
         # cold (primary): every byte comes from HBM; warm: back-to-back calls, part of the 1.06 GB may
         # still sit in the 256 MB last-level cache
-        wall, pk, pc = timed(fn, between=lambda: flush.sum())
-        rec = leg_record(pk, pc, wall, calls, "hbm", nbytes, ceil)
-        split = [n for n in pk if "split" in n][0]
+        tm = timed(fn, between=lambda: flush.sum())
+        rec = leg_record(tm, calls, "hbm", nbytes, ceil)
+        split = [n for n in tm["per_kernel"] if "split" in n][0]
         rec.update(compulsory_bytes=nbytes, cache="cold (1 GiB buffer read before each call, outside the timed "
                                                    "kernels and the call's events)",
                    split_kernel=rate_of("hbm", nbytes, rec["kernels"][split]["mean_ms"], ceil),
                    tflops=L.decode_flops(w.H, w.d, lens) / (rec["avg_ms"] * 1e-3) / 1e12, **extra)
-        wall_w, pk_w, pc_w = timed(fn)
-        warm = leg_record(pk_w, pc_w, wall_w, calls, "hbm", nbytes, ceil)
+        warm = leg_record(timed(fn), calls, "hbm", nbytes, ceil)
         rec["warm"] = {"avg_ms": warm["avg_ms"], "gbs": warm["gbs"], "frac_of_peak": warm["frac_of_peak"],
                        "kernels": warm["kernels"], "call_device_ms": warm["call_device_ms"]}
         legs[name] = rec
-        log(f"[bench] leg {name}: {rec['avg_ms']:.4f} ms over {len(pk)} kernel(s), {rec['gbs']:.0f} GB/s "
+        log(f"[bench] leg {name}: {rec['avg_ms']:.4f} ms over {len(tm['per_kernel'])} kernel(s), {rec['gbs']:.0f} GB/s "
             f"({rec['frac_of_peak']:.3f} of 8 TB/s whole call; split kernel {rec['split_kernel']['gbs']:.0f} GB/s); "
             f"warm {rec['warm']['gbs']:.0f} GB/s")
 

@@ -70,3 +70,19 @@ def test_rates_against_peak_and_ceiling():
 def test_committed_ceilings_without_measuring():
     c = bench.ceilings(False)
     assert c["mfma_bf16_tflops"] > 2000 and c["hbm_read_gbs"] > 6000 and "committed" in c["source"]
+
+
+def test_leg_time_source_and_rates():
+    """A leg's time per call: the back-to-back loop when there is one, else the per-call events (legs
+    with work between calls); the library timer's per-kernel durations are kept apart and never set
+    the rate."""
+    ceil = dict(bench.COMMITTED_CEILINGS)
+    base = {"per_call": [0.5] * 20 + [0.6] * 5, "per_kernel": {"k": [0.9] * 25}}
+    loop = bench.leg_record({**base, "wall_s": 0.02, "loop_ms": 10.0}, 25, "mfma", 1e12, ceil, "k")
+    assert loop["time_source"] == "back-to-back loop" and loop["avg_ms"] == 10.0 / 25
+    assert abs(loop["tflops"] - 1e12 / 0.4e-3 / 1e12) < 1e-9
+    assert loop["kernels_sum_ms"] == 0.9 and loop["loop_ms_per_call"] == 0.4
+    events = bench.leg_record({**base, "wall_s": None, "loop_ms": None}, 25, "hbm", 1e9, ceil)
+    assert events["time_source"] == "per-call events"
+    assert abs(events["avg_ms"] - (20 * 0.5 + 5 * 0.6) / 25) < 1e-12 and "loop_ms_per_call" not in events
+    assert abs(events["gbs"] - 1e9 / (events["avg_ms"] * 1e-3) / 1e9) < 1e-9
