@@ -99,6 +99,57 @@ struct DecodeMerge {
 // the KV head's rows again).
 constexpr int kDecodeAnyGroup = 16;
 
+// Work items of the split kernel: (split s, sequence b, KV head hk) for every split that holds keys,
+// enumerated split-major (split 0 of every sequence and KV head, then split 1, ...). Workgroup
+// `lin` in launch order takes item lin / n_chunk (n_chunk workgroups per item), and ids past the
+// last item exit. The workgroups that own no keys thus come after every working one in launch
+// order: spread among them, as they were with one workgroup per (split, sequence, KV head), each
+// held a dispatch slot while it read its length and exited, and freed CU slots sat empty for
+// microseconds (measured: a CU held on average 1.43 of its 2 workgroup slots over the kernel).
+// Computed by every wave from the lengths (one 4-byte load per lane and sequence); all results
+// are wave-uniform.
+struct DecodeItem {
+  int split, b, hk, len;
+};
+__device__ __forceinline__ bool decode_item(const int32_t* __restrict__ kv_len, int B, int H_kv, int N_cap,
+                                            int n_split, int item, DecodeItem& out) {
+  const int lane = threadIdx.x & 63;
+  auto n_splits_of = [&](int b) { return b < B ? (clamp_len(kv_len, b, N_cap) + kDecodeSplit - 1) / kDecodeSplit : 0; };
+  const int ns0 = n_splits_of(lane);  // the common case, B <= 64, needs no other load
+  int rem = item;
+  for (int s = 0; s < n_split; ++s) {
+    int cnt = 0;  // sequences with more than s splits
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int ns = b0 == 0 ? ns0 : n_splits_of(b0 + lane);
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ns > s));
+    }
+    if (rem < cnt * H_kv) {
+      const int j = rem / H_kv;  // the j-th such sequence, in order
+      int seen = 0;
+      for (int b0 = 0; b0 < B; b0 += 64) {
+        const int ns = b0 == 0 ? ns0 : n_splits_of(b0 + lane);
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(ns > s);
+        const int c = __builtin_popcountll(mask);
+        if (j < seen + c) {
+          // lane whose bit is set with exactly j - seen set bits below it
+          const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          const uint64_t hit = __builtin_amdgcn_ballot_w64(ns > s && below == j - seen);
+          const int b = b0 + (int)__builtin_ctzll(hit);
+          out.split = s;
+          out.b = b;
+          out.hk = rem % H_kv;
+          out.len = clamp_len(kv_len, b, N_cap);
+          return true;
+        }
+        seen += c;
+      }
+    }
+    rem -= cnt * H_kv;
+  }
+  return false;
+}
+
 template <int HD, int G, bool PAGED>
 __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
     const bf16* __restrict__ Qd, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
@@ -115,22 +166,24 @@ __global__ __launch_bounds__(DEC_WAVES * 64, 2) void decode_split_kernel(
   __shared__ bf16 vtile[DEC_WAVES][DEC_TILE * HD];
   __shared__ DecodeMerge<HD, G> mg;
 
-  // Grid (B * H_kv * n_chunk, n_split), x fastest: workgroups reach the 8 XCDs round-robin in
-  // launch order, so consecutive ids walk the (sequence, KV head, head chunk) triples of one split
+  // Grid (B * H_kv * n_chunk, n_split) in launch order (x fastest): workgroups reach the 8 XCDs
+  // round-robin, so consecutive ids walk the (sequence, KV head, head chunk) triples of one split
   // and every XCD gets an even share of each split. (With the split index fastest, split s would
   // always land on XCD s mod 8 and short sequences would load only the first few XCDs.)
   constexpr bool ANY = G == kDecodeAnyGroup;
-  const int split = blockIdx.y;
-  const int chunk = ANY ? (int)blockIdx.x % n_chunk : 0;
-  const int bk = ANY ? (int)blockIdx.x / n_chunk : (int)blockIdx.x;
-  const int hk = bk % H_kv;
-  const int b = bk / H_kv;
+  const int lin = (int)blockIdx.y * (int)gridDim.x + (int)blockIdx.x;
+  const int chunk = ANY ? lin % n_chunk : 0;
+  DecodeItem it;
+  if (!decode_item(kv_len, (int)gridDim.x / (H_kv * n_chunk), H_kv, N_cap, n_split, ANY ? lin / n_chunk : lin, it))
+    return;  // uniform over the workgroup, before any barrier
+  const int split = it.split;
+  const int hk = it.hk;
+  const int b = it.b;
   const int gsize = ANY ? grp : G;                                // query heads per KV head
   const int head0 = hk * gsize + 16 * chunk;                      // first query head of this workgroup
   const int gh = ANY ? min(16, gsize - 16 * chunk) : G;           // query heads of this workgroup
-  const int len = clamp_len(kv_len, b, N_cap);
+  const int len = it.len;
   const int k_begin = split * kDecodeSplit;
-  if (k_begin >= len) return;  // uniform over the workgroup, before any barrier
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
