@@ -115,9 +115,10 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
 /*
  * Decode: one query token per (sequence, head) against a KV cache, the regime of
  * "Why Fast GPUs Still Wait for Memory", section "Attention III - KV cache, GQA, MLA"
- * (I = 2g/s, memory-bound). The key range of each sequence is split across workgroups and a
- * second kernel merges the partial (max, sum, output) triples ("M4.2 - GPU Execution Model for
- * Transformer Kernels", section 0x08: split-K needs an extra reduction).
+ * (I = 2g/s, memory-bound). The keys of all sequences are split across workgroups in equal
+ * shares (a share may cover parts of several sequences) and a second kernel merges the partial
+ * (max, sum, output) triples ("M4.2 - GPU Execution Model for Transformer Kernels", section 0x08:
+ * split-K needs an extra reduction).
  *   q [B, H, d] bf16; k_cache, v_cache [B, H_kv, N_cap, d] bf16; o [B, H, d] bf16;
  *   lse [B, H] float32 or NULL; kv_len [B] int32 DEVICE array, sequence b attends to cache rows
  *   0 .. kv_len[b]-1 and never reads rows at or beyond kv_len[b]. Values are clamped to

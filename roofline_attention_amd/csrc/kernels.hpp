@@ -68,8 +68,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int B, int H, int H_kv, int N, int d, bool causal, float scale,
                           hipStream_t stream);
 
-// Decode split size (keys per workgroup) and workspace layout: per (b, h, split) a record of
-// d + 4 floats {m, l, -, -, o[0..d)} (m in log2 units of the scaled score, o not yet divided by l).
+// Decode: the least number of keys one split-kernel workgroup streams (its share of the batch's
+// keys is at least this long), and the workspace layout: per (b, h) ceil(N_cap / kDecodeSplit) + 1
+// record slots of d + 4 floats {m, l, np, -, o[0..d)} (m in log2 units of the scaled score, o not
+// yet divided by l, np the segment's record count as int bits), one per workgroup share that meets
+// the segment.
 #ifndef RA_DECODE_SPLIT
 #define RA_DECODE_SPLIT 1024
 #endif

@@ -162,7 +162,7 @@ def test_bwd_varlen_validation(lib):
 def test_decode_validation(lib):
     p = [addr(i) for i in range(7)]
     ws_need = lib.attn_decode_workspace_size(64, 32, 8192, 128)
-    assert ws_need == 64 * 32 * 8 * (128 + 4) * 4  # 1024-key splits
+    assert ws_need == 64 * 32 * 9 * (128 + 4) * 4  # ceil(8192 / 1024) + 1 record slots
 
     def call(B=64, H=32, H_kv=8, N_cap=8192, d=128, dtype=BF16, ws=p[6], ws_bytes=ws_need, kv=p[5]):
         return lib.attn_decode(p[0], p[1], p[2], p[3], p[4], kv, B, H, H_kv, N_cap, d, 0, 0.088, dtype, ws,
@@ -188,7 +188,7 @@ def test_decode_noalloc_validation(lib):
         q = ptrs if ptrs is not None else p
         return lib.attn_decode_noalloc(*q, B, H, H_kv, N_cap, d, 0, 0.088, dtype, None)
 
-    assert call(N_cap=16384) == WORKSPACE  # 64 x 32 x 16 splits x 528 B = 17.3 MB
+    assert call(N_cap=16384) == WORKSPACE  # 64 x 32 x 17 record slots x 528 B = 18.4 MB
     assert b"scratch" in lib.attn_last_error()
     assert call(d=96) == UNSUPPORTED
     assert call(dtype=F32) == UNSUPPORTED

@@ -303,10 +303,54 @@ def test_decode_ragged_lengths(lib, H, H_kv, d):
 
 
 def test_decode_more_than_64_splits(lib):
-    # 69 and 65 splits of 1024 keys: the merge takes more than one 64-lane pass over the splits.
+    # About 69 and 65 partial records per (sequence, head) (every workgroup share holds at least
+    # 1024 keys): the merge takes more than one 64-lane pass over the records.
     w = I.Workload("dec_long", "decode", 2, 8, 2, 70000, 64, "bf16", False, seed=18, kv_lo=1, kv_hi=70000)
     eo, el = decode_check(lib, w, kv_len=[70000, 65601])
     assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
+def decode_check_with_empty(lib, w, lens):
+    """Decode with the given lengths (zeros allowed): empty sequences give O = 0 and LSE = -inf
+    exactly, the others match the oracle."""
+    t = I.make_decode(w, nan_pad=False)
+    t["kv_len"] = torch.tensor(lens, dtype=torch.int32)
+    for b in range(w.B):
+        t["k"][b, :, lens[b]:] = float("nan")
+        t["v"][b, :, lens[b]:] = float("nan")
+    o, lse = lib.decode(dev(t["q"]), dev(t["k"]), dev(t["v"]), dev(t["kv_len"]), w.scale)
+    o, lse = o.cpu(), lse.cpu()
+    q = f64(t["q"])
+    err = 0.0
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.count_nonzero(o[b]) == 0 and bool(torch.all(lse[b] == -float("inf")))
+            continue
+        ro, rl = orc.attention_decode(q[b:b + 1], f64(t["k"][b:b + 1, :, :n]), f64(t["v"][b:b + 1, :, :n]),
+                                      np.array([n]), w.scale)
+        err = max(err, float(np.max(np.abs(f64(o[b:b + 1]) - ro))), float(np.max(np.abs(f64(lse[b:b + 1]) - rl))))
+    return err
+
+
+def test_decode_one_share_over_many_short_sequences(lib):
+    # 40 sequences of 0..40 keys over 2 KV heads: fewer than 1024 keys in all, so one workgroup
+    # takes every segment, one piece (and one merge) after another, empty sequences skipped.
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(0, 41, size=40)]
+    lens[3] = lens[17] = 0
+    w = I.Workload("dec_short", "decode", 40, 8, 2, 64, 128, "bf16", False, seed=41, kv_lo=0, kv_hi=40)
+    assert decode_check_with_empty(lib, w, lens) <= TOL_BF16
+
+
+def test_decode_more_than_64_sequences(lib):
+    # 130 sequences (three 64-lane chunks of the length scan) with mixed lengths, zeros included:
+    # workgroup shares start and end inside sequences of every chunk.
+    rng = np.random.default_rng(42)
+    lens = [int(x) for x in rng.integers(0, 2500, size=130)]
+    lens[0] = lens[64] = lens[129] = 0
+    lens[63], lens[65] = 2500, 1
+    w = I.Workload("dec_many", "decode", 130, 8, 4, 2500, 64, "bf16", False, seed=42, kv_lo=0, kv_hi=2500)
+    assert decode_check_with_empty(lib, w, lens) <= TOL_BF16
 
 
 @pytest.mark.parametrize("page_size", [32, 64, 256])
@@ -345,8 +389,8 @@ def test_decode_paged_full_workload_matches_dense(lib):
 
 def test_decode_workspace_reuse_with_other_inputs(lib):
     # One workspace serves calls on different inputs (contiguous and paged, one sequence of length
-    # 0, lengths on both sides of the 1024-key split): each call's records are written before the
-    # merge reads them, so no call sees another's partial results.
+    # 0, lengths on both sides of 1024 keys): each call's records, piece counts included, are
+    # written before the merge reads them, so no call sees another's partial results.
     lens = [5000, 1, 1024, 1025, 3333, 0]
     cases = []
     for seed in (19, 20):

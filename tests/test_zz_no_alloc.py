@@ -78,7 +78,7 @@ def test_noalloc_matches_decode_on_two_calls_the_second_smaller(lib):
 
 def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     raw = lib.raw()
-    # 64 x 32 heads x 16 splits (16k keys) x 132 floats = 17.3 MB of records > 16 MiB: rejected
+    # 64 x 32 heads x 17 record slots (16k keys) x 132 floats = 18.4 MB of records > 16 MiB: rejected
     # before any device work (the pointers are never dereferenced)
     B, H, H_kv, N, d = 64, 32, 8, 16384, 128
     assert raw.attn_decode_workspace_size(B, H, N, d) > SCRATCH
@@ -86,7 +86,7 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(lib):
     st = raw.attn_decode_noalloc(*fake, B, H, H_kv, N, d, 0, 0.088, 1, None)
     assert st == 3 and b"scratch" in raw.attn_last_error()  # ATTN_ERR_WORKSPACE
     # the binding reports it as an error too
-    # 64 query heads over 1M cache rows at d = 64: 64 x 1024 splits x 68 floats = 17.8 MB of records
+    # 64 query heads over 1M cache rows at d = 64: 64 x 1025 record slots x 68 floats = 17.8 MB of records
     assert raw.attn_decode_workspace_size(1, 64, 1 << 20, 64) > SCRATCH
     q = torch.zeros((1, 64, 64), dtype=torch.bfloat16, device="cuda")
     kc = torch.zeros((1, 8, 1 << 20, 64), dtype=torch.bfloat16, device="cuda")
