@@ -281,6 +281,17 @@ def rate_of(kind, amount, ms, ceil):
     return {"gbs": r, "frac_of_peak": r / L.PEAK_HBM_GBS, "frac_of_ceiling": r / ceil["hbm_read_gbs"]}
 
 
+def roofline_time(flops, peak_tflops, nbytes, ms):
+    """The roofline time of one call, max(work / matrix peak, compulsory bytes / HBM peak), which of the
+    two bounds it, and the measured time's fraction of it (1.0 = at the roofline)."""
+    from roofline_attention_amd import ledger as L
+    t_mfma = flops / (peak_tflops * 1e12) * 1e3
+    t_hbm = nbytes / (L.PEAK_HBM_GBS * 1e9) * 1e3
+    t = max(t_mfma, t_hbm)
+    return {"bound": "mfma" if t_mfma >= t_hbm else "hbm", "mfma_ms": t_mfma, "hbm_ms": t_hbm,
+            "compulsory_bytes": nbytes, "frac": t / ms}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -435,13 +446,16 @@ def run_legs(torch, lib, I, L, ceil, calls=LEG_CALLS):
         tm = timed(call)
         (kname,) = tm["per_kernel"]
         legs[name] = leg_record(tm, calls, "mfma", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), ceil, kname)
+        legs[name]["roofline"] = roofline_time(L.fwd_flops(w.B, w.H, w.N, w.d, w.causal), L.PEAK_BF16_TFLOPS,
+                                               L.fwd_bytes(w.B, w.H, w.H_kv, w.N, w.d, 2), legs[name]["avg_ms"])
         if name == "prefill_causal_1k":
             # a launch-bound call: the same calls replayed from a HIP graph, for comparison
             g = dist(time_graph(torch, call, calls))
             legs[name]["graph_replay"] = {"ms_per_call": g, **rate_of("mfma", L.fwd_flops(w.B, w.H, w.N, w.d, w.causal),
                                                                        g["mean_ms"], ceil)}
         log(f"[bench] leg {name}: {legs[name]['avg_ms']:.4f} ms ({legs[name]['time_source']}), "
-            f"{legs[name]['tflops']:.1f} TFLOP/s")
+            f"{legs[name]['tflops']:.1f} TFLOP/s, {legs[name]['roofline']['frac']:.3f} of its roofline "
+            f"({legs[name]['roofline']['bound']}-bound)")
         del t, o, lse
         torch.cuda.empty_cache()
 

@@ -86,3 +86,19 @@ def test_leg_time_source_and_rates():
     assert events["time_source"] == "per-call events"
     assert abs(events["avg_ms"] - (20 * 0.5 + 5 * 0.6) / 25) < 1e-12 and "loop_ms_per_call" not in events
     assert abs(events["gbs"] - 1e9 / (events["avg_ms"] * 1e-3) / 1e9) < 1e-9
+
+
+def test_roofline_time_names_the_binding_resource():
+    from roofline_attention_amd import ledger as L
+    # [4,16,1024,64] causal bf16: 8.6 GFLOP (3.4 us at the bf16 peak) but 33.8 MB of compulsory
+    # traffic (4.2 us at 8 TB/s), so the HBM bound sets its roofline
+    fl = L.fwd_flops(4, 16, 1024, 64, True)
+    by = L.fwd_bytes(4, 16, 16, 1024, 64, 2)
+    r = bench.roofline_time(fl, L.PEAK_BF16_TFLOPS, by, 0.0184)
+    assert r["bound"] == "hbm"
+    assert abs(r["hbm_ms"] - by / 8e12 * 1e3) < 1e-12 and r["hbm_ms"] > r["mfma_ms"]
+    assert abs(r["frac"] - r["hbm_ms"] / 0.0184) < 1e-12
+    # [2,32,4096,128] causal: compute-bound
+    r = bench.roofline_time(L.fwd_flops(2, 32, 4096, 128, True), L.PEAK_BF16_TFLOPS,
+                            L.fwd_bytes(2, 32, 32, 4096, 128, 2), 0.26)
+    assert r["bound"] == "mfma" and 0.4 < r["frac"] < 0.45
