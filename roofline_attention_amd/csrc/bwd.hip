@@ -32,7 +32,7 @@ namespace ra {
 namespace {
 
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(BWD_THREADS, dkdv_waves_per_simd<HD>()) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, int H, int group, int N, int n_ktiles, float scale,
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(BWD_THREADS, RA_DQ_WAVES_PER_SIMD) void bwd_dq_kern
 // are dealt round-robin over the XCDs, as in the ragged forward, so that every XCD gets an equal
 // share of every sequence.
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(BWD_THREADS, RA_DKDV_WAVES_PER_SIMD) void bwd_dkdv_varlen_kernel(
+__global__ __launch_bounds__(BWD_THREADS, dkdv_waves_per_simd<HD>()) void bwd_dkdv_varlen_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, const int32_t* __restrict__ cu_seqlens, int T, int H,

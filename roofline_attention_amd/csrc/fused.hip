@@ -73,7 +73,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void fwdbwd_kernel(
     __syncthreads();  // every wave has read s_item before thread 0 takes the next one
     if (j >= n_col_items) break;
     const int item = (j % n_bhk) * n_t + j / n_bhk;  // the key-major item numbering: bhk * n_t + kt
-    bwd_dkdv_job<HD, CAUSAL, false, false>(Q, K, V, dO, L2, Dg, dK, dV, H, group, N, n_t, scale, scale_log2,
+    bwd_dkdv_job<HD, CAUSAL, false, false, false>(Q, K, V, dO, L2, Dg, dK, dV, H, group, N, n_t, scale, scale_log2,
                              *reinterpret_cast<DkdvSmem<HD>*>(dyn_smem), item);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // LDS stages free for the next item
