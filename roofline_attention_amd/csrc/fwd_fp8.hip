@@ -20,13 +20,18 @@
 //   * K and V tiles (d-byte rows) go straight from HBM into LDS, 16-byte chunks XOR-swizzled so
 //     that the K row reads (16 rows per b128 phase) and the transposed V reads (8 rows x 2 chunks
 //     per 32 lanes) hit distinct banks.
-//   * P is formed as 2^(s - m + 6) with the running maximum m raised only when a tile's maximum
-//     exceeds it by more than 2 (log2 units): P then lies in (0, 2^8], inside E4M3's finite range,
-//     and every P down to 2^-12 of the running maximum is a normal E4M3 number.
+//   * P is formed as 2^(s - m + 6), the reference m always some tile's maximum (so at most the
+//     row's): every P down to 2^-12 of it is a normal E4M3 number.
 //   * The normaliser is the sum of the E4M3-rounded P, the values that multiply V, and it is taken
 //     on the matrix core: one more 64-key MFMA per tile, with an all-ones A operand, leaves every
 //     lane the column sum of its query. The kernel is bound by its vector work, not by the matrix
 //     core, so one MFMA (64 cycles) in place of 31 float32 adds per lane is a net gain.
+//   * The probabilities are taken against the current reference first. The E4M3 conversion does not
+//     saturate (a value above 464 becomes the NaN code) and the matrix unit carries a NaN byte into
+//     its query's column sum, so a NaN sum flags a probability that does not fit; only then (and on
+//     a row's first tile) does the tile compute its maximum, raise the reference when the maximum
+//     exceeds it by more than 2 (log2 units), rescale O and take the probabilities again. Every P
+//     that multiplies V is a finite E4M3 value of at most 448.
 //   * Descales: q and k descales fold into the score factor, the v descale into the final 1 / l.
 #include <float.h>
 #include <math.h>
@@ -254,14 +259,14 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
         pf[i] = word;
       }
     };
-    // Normaliser update: the tile's sum of the E4M3 probabilities of this lane's query, as the
-    // product of an all-ones 32 x 64 block (E4M3 1.0 = 0x38) with P^T; every element of the result
-    // holds the column sum, so element 0 is taken.
-    auto norm = [&](const i32x8& pf, float alpha) {
+    // The tile's sum of the E4M3 probabilities of this lane's query, as the product of an all-ones
+    // 32 x 64 block (E4M3 1.0 = 0x38) with P^T; every element of the result holds the column sum,
+    // so element 0 is taken. The conversion does not saturate: a probability above 464 becomes the
+    // E4M3 NaN code, and the matrix unit carries it into its query's sum (both measured on gfx950).
+    auto colsum = [&](const i32x8& pf) {
       const int one4 = 0x38383838;
       const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
-      const f32x16 colsum = mfma_f8(ones, pf, f32x16{});
-      l_run = fmaf(l_run, alpha, colsum[0]);
+      return mfma_f8(ones, pf, f32x16{})[0];
     };
 
     // O^T += V^T P^T: one 64-key MFMA per 32 output columns.
@@ -294,6 +299,12 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
     scores(sm.k[0], s_cur);
     __syncthreads();  // every wave has read K0 before its stage is reused for K2
 
+    // Online-softmax step of tile kt. The probabilities are first taken against the current
+    // reference, and while every one of them stays finite in E4M3 (no column sum is NaN) that
+    // reference serves: no maximum, no rescale. Otherwise (a probability above 464, the reference
+    // still unset, or a NaN score) the exact step runs: tile maximum, the lazy raise decision,
+    // rescale of O, probabilities again. Every reference is some tile's maximum, at most the row's
+    // maximum, and every probability that multiplies V is a finite E4M3 value at most 448.
     // Entering step kt: sc = S^T of tile kt, K_{kt+1} and V_kt in LDS. Issues V_{kt+1} and K_{kt+2},
     // the score MFMAs of tile kt+1 beside the softmax of tile kt, then O += V_kt P_kt.
     auto step = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
@@ -301,32 +312,42 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       if (kt + 2 < n_kt) issue_k(kt + 2, kt & 1);
       if (is_boundary(kt)) apply_mask(kt * F8_BC, sc);
       i32x8 pf;
-      float alpha;
-      // As in the bf16 forward: the maximum goes with the first half of tile kt+1's score MFMAs
-      // before the rescale branch, the exponentials with the second half and O += V P after it.
+      // The first half of tile kt+1's score MFMAs goes with the exponentials, the second half
+      // after the (rare) exact branch, then O += V P.
       scores_half(sm.k[(kt + 1) & 1], sn, 0);
-      if (decide(sc, alpha)) {
+      probs(sc, pf);
+      float cs = colsum(pf);
+      float alpha = 1.f;
+      if (__builtin_amdgcn_ballot_w64(__builtin_isnan(cs)) != 0) {
+        if (decide(sc, alpha)) {
 #pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+          for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+        }
+        probs(sc, pf);
+        cs = colsum(pf);
       }
       scores_half(sm.k[(kt + 1) & 1], sn, 1);
-      probs(sc, pf);
+      l_run = fmaf(l_run, alpha, cs);
       pv(sm.v[kt & 1], pf);
-      norm(pf, alpha);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
     auto last = [&](int kt, f32x16 (&sc)[2]) {
       if (is_boundary(kt)) apply_mask(kt * F8_BC, sc);
       i32x8 pf;
-      float alpha;
-      if (decide(sc, alpha)) {
-#pragma unroll
-        for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
-      }
       probs(sc, pf);
+      float cs = colsum(pf);
+      float alpha = 1.f;
+      if (__builtin_amdgcn_ballot_w64(__builtin_isnan(cs)) != 0) {
+        if (decide(sc, alpha)) {
+#pragma unroll
+          for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
+        }
+        probs(sc, pf);
+        cs = colsum(pf);
+      }
+      l_run = fmaf(l_run, alpha, cs);
       pv(sm.v[kt & 1], pf);
-      norm(pf, alpha);
     };
     f32x16 s_alt[2];
     int kt = 0;
@@ -334,12 +355,20 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
       step(kt, s_cur, s_alt);
       step(kt + 1, s_alt, s_cur);
     }
+    // One last() on one buffer (two inlined copies cost registers around the exact branch).
     if (kt + 1 < n_kt) {
       step(kt, s_cur, s_alt);
-      last(kt + 1, s_alt);
-    } else {
-      last(kt, s_cur);
+      s_cur[0] = s_alt[0];
+      s_cur[1] = s_alt[1];
+      ++kt;
     }
+    last(kt, s_cur);
+    // The output accumulators are complete here, before the lane-divergent store below: left to
+    // itself the compiler sinks the last tile's O += V P into that branch, where the matrix
+    // instruction runs with the rows past N switched off in EXEC and returns wrong sums for the
+    // other rows of the wave (measured).
+#pragma unroll
+    for (int cb = 0; cb < CBLK; ++cb) asm volatile("" : "+v"(oacc[cb]));
 
     if (qi < N) {
       const float inv = v_descale / l_run;
