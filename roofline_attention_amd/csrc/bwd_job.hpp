@@ -553,15 +553,39 @@ __device__ __forceinline__ void bwd_dq_job(
       for (int kb = 0; kb < 2; ++kb) {
         // S^T and dP^T: lane column = query, rows = keys k0 + 32kb + 8(r/4) + 4g + r%4. The first
         // k-step takes a zero accumulator operand directly (no zero-filled registers).
+        // Each MFMA's LDS operand is read two MFMAs ahead; the empty asm statements (memory
+        // clobbers) keep the compiler from sinking the reads back next to their MFMAs, where each
+        // would wait out its own LDS latency. (Measured with the dQ product's reads below:
+        // [2,16,4096,128] causal dQ 0.200 -> 0.193 ms, d = 64 shapes 1.5-6% faster, results bitwise
+        // equal.)
         const bf16* krow = sm.k[s] + kb * 32 * HD + row_off;
         const bf16* vrow = sm.v[s] + kb * 32 * HD + row_off;
-        f32x16 sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + (0 ^ krow_t) * 8), qf[0], f32x16{});
-        f32x16 dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + (0 ^ vrow_t) * 8), df[0], f32x16{});
+        constexpr int PF = 2;
+        auto rd_row = [&](int i) {  // operand of MFMA i: S^T (i even) or dP^T (i odd), k-step i / 2
+          const int kk = i >> 1;
+          return (i & 1) ? *reinterpret_cast<const bf16x8*>(vrow + ((2 * kk) ^ vrow_t) * 8)
+                         : *reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ krow_t) * 8);
+        };
+        bf16x8 opa[PF];
 #pragma unroll
-        for (int kk = 1; kk < KSTEPS; ++kk) {
-          sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ krow_t) * 8), qf[kk], sacc);
-          dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + ((2 * kk) ^ vrow_t) * 8), df[kk], dpacc);
+        for (int i = 0; i < PF; ++i) opa[i] = rd_row(i);
+        asm volatile("" ::: "memory");
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int i = 0; i < 2 * KSTEPS; ++i) {
+          const int kk = i >> 1;
+          if (i & 1) dpacc = mfma32(opa[i % PF], df[kk], dpacc);
+          else sacc = mfma32(opa[i % PF], qf[kk], sacc);
+          if (i + PF < 2 * KSTEPS) opa[i % PF] = rd_row(i + PF);
+          asm volatile("" ::: "memory");
         }
+        // The dQ product's first K^T operands do not depend on dS: read them before the vector work.
+        constexpr int PFB = 4;
+        auto rd_tr = [&](int i) { return tr_operand<HD>(sm.k[s], tl, 32 * kb + 16 * (i / CBLK), i % CBLK); };
+        bf16x8 opb[PFB];
+#pragma unroll
+        for (int i = 0; i < PFB; ++i) opb[i] = rd_tr(i);
+        asm volatile("" ::: "memory");
         bf16x8 dsb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -570,12 +594,12 @@ __device__ __forceinline__ void bwd_dq_job(
           dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - Dq));
         }
         // dQ^T += K^T dS^T for this block's 32 keys: A = K^T (rows c = 32cb + l32 by transposed
-        // read of the key tile), k-steps 2kb, 2kb + 1.
+        // read of the key tile), k-steps 2kb, 2kb + 1; MFMA i takes k-step i / CBLK, block i % CBLK.
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-          for (int cb = 0; cb < CBLK; ++cb)
-            acc[cb] = mfma32(tr_operand<HD>(sm.k[s], tl, 32 * kb + 16 * hh, cb), dsb[hh], acc[cb]);
+        for (int i = 0; i < 2 * CBLK; ++i) {
+          acc[i % CBLK] = mfma32(opb[i % PFB], dsb[i / CBLK], acc[i % CBLK]);
+          if (i + PFB < 2 * CBLK) opb[i % PFB] = rd_tr(i + PFB);
+          asm volatile("" ::: "memory");
         }
       }
     };
