@@ -250,13 +250,30 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       }
     };
 
-    // One 32-key half (block kb) of S^T for one tile.
+    // One 32-key half (block kb) of S^T for one tile. At d = 128 each K operand is read two MFMAs
+    // ahead, pinned there by empty asm statements with memory clobbers (the compiler otherwise
+    // places some reads right before their MFMA, which then waits the LDS latency): about 1%
+    // on the 4k shapes, bitwise the same; at d = 64 it measured 0.3-0.6% slower.
     auto scores_half = [&](const bf16* kbuf, f32x16 (&s)[2], int kb) {
       s[kb] = f32x16{};
       const bf16* krow = &kbuf[32 * kb * HD + k_lane];
+      if constexpr (HD == 128) {
+        constexpr int SPF = 2;
+        bf16x8 op[SPF];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ k_t) * 8), qf[kk], s[kb]);
+        for (int i = 0; i < SPF; ++i) op[i] = *reinterpret_cast<const bf16x8*>(krow + ((2 * i) ^ k_t) * 8);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          s[kb] = mfma32(op[kk % SPF], qf[kk], s[kb]);
+          if (kk + SPF < KSTEPS) op[kk % SPF] = *reinterpret_cast<const bf16x8*>(krow + ((2 * (kk + SPF)) ^ k_t) * 8);
+          asm volatile("" ::: "memory");
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(krow + ((2 * kk) ^ k_t) * 8), qf[kk], s[kb]);
+      }
     };
 
     f32x16 oacc[CBLK];
@@ -338,7 +355,28 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
     };
 
     // O^T += V^T P^T. A operand: lane row c = 32cb + l32, keys 32kb + 16hh + {4g..4g+3, 8+4g..8+4g+3}.
+    // At d = 64 the V^T operands are read four MFMAs ahead (pinned as above): 3% on [4,16,1024,64]
+    // causal, bitwise the same; at d = 128 no gain.
     auto pv = [&](const bf16* vbuf, const bf16x8 (&pf)[4]) {
+      if constexpr (HD == 64) {
+        constexpr int VPF = 4;
+        auto rdv = [&](int i) {  // operand of MFMA i: k-step i / CBLK, output block i % CBLK
+          const int ks = i / CBLK, cb = i % CBLK;
+          const bf16* vp = &vbuf[(32 * (ks >> 1) + 16 * (ks & 1)) * HD + v_lane + ((4 * cb) ^ v_t) * 8];
+          return __builtin_shufflevector(lds_read_tr(vp), lds_read_tr(vp + 8 * HD), 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 op[VPF];
+#pragma unroll
+        for (int i = 0; i < VPF; ++i) op[i] = rdv(i);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 4 * CBLK; ++i) {
+          oacc[i % CBLK] = mfma32(op[i % VPF], pf[i / CBLK], oacc[i % CBLK]);
+          if (i + VPF < 4 * CBLK) op[i % VPF] = rdv(i + VPF);
+          asm volatile("" ::: "memory");
+        }
+        return;
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int kb = ks >> 1;
