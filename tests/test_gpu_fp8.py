@@ -245,3 +245,52 @@ def test_fp8_prefill_16k_sampled_rows(lib):
     flat = np.concatenate([np.stack([np.full(len(ii), b), np.full(len(ii), h), ii], 1) for b, h, ii in rows_by_head])
     ro, rl = orc.attention_fwd_fp8_rows(t["q"].numpy(), t["k"].numpy(), t["v"].numpy(), ds, w.causal, w.scale, flat)
     check(o, lse, q, k, v, w.causal, w.scale, rows_by_head, ro, rl, "fp8_16k")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_rising_scores_take_both_softmax_paths(lib, causal):
+    """Scores that rise from one 64-key tile to the next by 1.4 to 2.9 (log2 units): a rise of at
+    most 2.86 leaves every probability finite in E4M3 (up to 2^8.86) on the path without the row
+    maximum, a larger one overflows E4M3, turns a column sum NaN and takes the exact step. Every
+    element stays within the derived bound, and the output is finite."""
+    w = I.Workload("fp8_rise", "fwd", 1, 2, 2, 512, 128, "e4m3", causal, seed=25)
+    t = I.make_fp8_prefill(w)
+    # key tile j carries the exact E4M3 value ramp[j] in dimension 0, every query 1.0 there; scale 1
+    ramp_codes = [0x00, 0x3C, 0x44, 0x48, 0x4C, 0x50, 0x52, 0x54]
+    ramp_vals = [0.0, 1.5, 3.0, 4.0, 6.0, 8.0, 10.0, 12.0]
+    assert np.array_equal(orc.e4m3_decode(np.array(ramp_codes, dtype=np.uint8)), np.array(ramp_vals))
+    rises = np.diff(np.array(ramp_vals)) * 1.4426950408889634
+    assert (rises <= 2.86).any() and (rises > 2.86).any() and (rises > 2.0).sum() >= 3
+    # noise: dimensions 1..8 of every key hold random E4M3 values in [-1/2, 1/2] (every such code),
+    # so scores within a tile are spread and their roundings behave as independent
+    small = np.array([c for c in range(256) if c != 0x80 and abs(orc.e4m3_decode(np.array([c], dtype=np.uint8))[0]) <= 0.5
+                      and np.isfinite(orc.e4m3_decode(np.array([c], dtype=np.uint8))[0])], dtype=np.uint8)
+    rng = np.random.default_rng(5)
+    q = torch.zeros_like(t["q"])
+    q[..., 0:9] = 0x38
+    k = torch.zeros_like(t["k"])
+    for j in range(8):
+        k[:, :, 64 * j:64 * j + 64, 0] = ramp_codes[j]
+    k[..., 1:9] = torch.from_numpy(rng.choice(small, size=tuple(k.shape[:3]) + (8,)))
+    case = {"q": q, "k": k, "v": t["v"], "descale": (1.0, 1.0, t["descale"][2])}
+    # The reference the kernel keeps per row: the first tile's maximum, raised (by more than 2) to a
+    # tile's maximum only when some 2^(s c - m + 6) of that tile does not fit E4M3 (above 464). All
+    # queries here score every key alike, so outside the diagonal tile a wave's rows decide alike and
+    # the per-row count below is the kernel's. Both outcomes occur.
+    sc = (orc.e4m3_decode(q.numpy()) @ np.swapaxes(orc.e4m3_decode(k.numpy()), -1, -2)) * 1.4426950408889634
+    fast_above_2 = exact_raise = 0
+    for row in sc.reshape(-1, w.N, w.N):
+        for i, srow in enumerate(row):
+            n_keys = i + 1 if causal else w.N
+            tiles = [srow[j:min(j + 64, n_keys)].max() for j in range(0, n_keys, 64)]
+            m = tiles[0]
+            for tm in tiles[1:]:
+                if tm - m > np.log2(464.0) - 6:
+                    exact_raise += 1
+                    m = tm if tm > m + 2 else m
+                elif tm - m > 2:
+                    fast_above_2 += 1
+    assert fast_above_2 > 0 and exact_raise > 0, (fast_above_2, exact_raise)
+    o, lse = run(lib, case, causal, 1.0)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    full_check(lib, case, causal, 1.0, case["descale"], f"fp8 rising scores causal={causal}")
