@@ -12,12 +12,13 @@
 // Kernels, per (batch, head), in this order:
 //   bwd_dq  : workgroup = 128 queries (4 waves x 32, Q and dO of its rows in registers); first the
 //             rows' D_i = sum_t dO[i,t] O[i,t] (equals sum_j P_ij dP_ij) and LSE_i log2 e, written
-//             out for the key-major kernel; then it streams 64-key tiles of K and V: S^T = K Q^T,
+//             out (D negated) for the key-major kernel; then it streams 64-key tiles of K and V: S^T = K Q^T,
 //             P^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T; stores dQ * scale.
 //   bwd_dkdv: workgroup = 128 keys (4 waves x 32, K and V of its keys in registers); streams
 //             64-query tiles of Q, dO, LSE and D through three LDS stages:
 //             S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e), dV += P^T dO, dP = dO V^T,
-//             dS = P (dP - D), dK += dS^T Q; stores dK * scale and dV.
+//             dS = P (dP - D), dK += dS^T Q; stores dK * scale and dV. Its dP accumulators start
+//             at the stored -D, so dS takes one multiply per element.
 // MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to bf16 (nearest
 // even) as MFMA operands. The probabilities and dS come out of the score accumulators already in
 // the A/B-operand layout their next product needs. Operands that contract over the rows of a

@@ -209,9 +209,24 @@ __device__ __forceinline__ void bwd_dkdv_job(
     // LDS latency: one wave per SIMD).
     struct AOps {
       bf16x8 q[KSTEPS], d[KSTEPS];
+      f32x16 dn;
+    };
+    // -D of the block's 32 query rows in the dP accumulator layout (rows 32u + 8(r/4) + 4g + r%4): the
+    // dP accumulators start there, so they end at dP - D and dS = P (dP - D) is one multiply.
+    auto load_dn = [&](int u) {
+      const float* dd = &sm.dd[stage_of(u >> 1)][(u & 1) * 32 + 4 * g];
+      f32x16 dn;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + 8 * rg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dn[4 * rg + e] = d4[e];
+      }
+      return dn;
     };
     auto load_A = [&](int u, AOps& op) {
       const int s = stage_of(u >> 1);
+      op.dn = load_dn(u);
       const bf16* qrow = sm.q[s] + (u & 1) * 32 * HD + row_off;
       const bf16* drow = sm.dO[s] + (u & 1) * 32 * HD + row_off;
 #pragma unroll
@@ -223,7 +238,7 @@ __device__ __forceinline__ void bwd_dkdv_job(
     };
     auto mfma_A = [&](const AOps& op, f32x16& sacc, f32x16& dpacc) {
       sacc = mfma32(op.q[0], kf[0], f32x16{});
-      dpacc = mfma32(op.d[0], vf[0], f32x16{});
+      dpacc = mfma32(op.d[0], vf[0], op.dn);
 #pragma unroll
       for (int kk = 1; kk < KSTEPS; ++kk) {
         sacc = mfma32(op.q[kk], kf[kk], sacc);
@@ -235,7 +250,7 @@ __device__ __forceinline__ void bwd_dkdv_job(
       const bf16* qrow = sm.q[s] + (u & 1) * 32 * HD + row_off;
       const bf16* drow = sm.dO[s] + (u & 1) * 32 * HD + row_off;
       sacc = f32x16{};
-      dpacc = f32x16{};
+      dpacc = load_dn(u);
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
         const int off = ((2 * kk) ^ row_t) * 8;
@@ -252,14 +267,13 @@ __device__ __forceinline__ void bwd_dkdv_job(
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse[s][qb * 32 + 8 * rg + 4 * g]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dd[s][qb * 32 + 8 * rg + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
           float p = fast_exp2(fmaf(sacc[r], scale_log2, -l4[e]));  // l4: LSE * log2 e
           if (mask && key > 32 * u + 8 * rg + 4 * g + e) p = 0.f;
           pb[r >> 3][r & 7] = to_bf16(p);
-          dsb[r >> 3][r & 7] = to_bf16(p * (dpacc[r] - d4[e]));
+          dsb[r >> 3][r & 7] = to_bf16(p * dpacc[r]);  // dpacc = dP - D (started at -D)
         }
       }
     };
@@ -503,7 +517,7 @@ __device__ __forceinline__ void bwd_dq_job(
           for (int e = 0; e < 8; ++e) Dq = fmaf(to_f32(a[e]), to_f32(df[kk][e]), Dq);
         }
       } else {
-        Dq = Dg[rowbase + qi];
+        Dq = -Dg[rowbase + qi];  // the workspace holds -D_i
       }
     } else {
 #pragma unroll
@@ -512,7 +526,7 @@ __device__ __forceinline__ void bwd_dq_job(
     if constexpr (ROW_TERMS) {
       Dq += __shfl_xor(Dq, 32, 64);  // the other half of the row (lane l32 + 32)
       if (qi < Nb && g == 0) {
-        Dg[rowbase + qi] = Dq;
+        Dg[rowbase + qi] = -Dq;  // stored negated: the key-major job starts its dP accumulators there
         L2[rowbase + qi] = lse2;  // the row's LSE in log2 units, streamed by the key-major job
       }
     }

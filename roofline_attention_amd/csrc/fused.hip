@@ -8,7 +8,7 @@
 //
 //   phase 1, one item per pair of query tiles (the causal pairing of the forward): the forward of
 //            the tiles (O, LSE), whose epilogue also writes the backward's per-row inputs
-//            D_i = sum_c dO[i,c] O[i,c] and LSE_i log2 e; then, in the same workgroup, dQ of the
+//            D_i = sum_c dO[i,c] O[i,c] (stored negated) and LSE_i log2 e; then, in the same workgroup, dQ of the
 //            same rows (it needs only those rows' LSE and D, just written by this workgroup);
 //   grid barrier (cooperative launch: every workgroup of the grid is resident at once);
 //   phase 2, one item per 128-key tile, heaviest (earliest under a causal mask) first, taken from

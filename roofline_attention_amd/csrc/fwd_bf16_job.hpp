@@ -282,14 +282,19 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
     float m_run = -INFINITY;  // reference maximum (log2 units) shared by numerator and normaliser
     float l_run = 0.f;        // this lane's share of the normaliser
 
-    // Masks raw scores of a boundary tile with -inf (causal diagonal, sequence end).
+    // Masks raw scores of a boundary tile with -inf (causal diagonal, sequence end). Slot (kb, r) of
+    // this lane holds key k0 + 4g + off(kb, r), off a compile-time constant below 64, and a key is
+    // kept when it is at most the lane's last visible key (its query row under the causal mask, and
+    // never past the sequence end): one compare against a lane threshold and one select per score.
     auto apply_mask = [&](int k0, f32x16 (&s)[2]) {
+      const int last_key = CAUSAL ? min(qi, Nb - 1) : Nb - 1;
+      const int lim = last_key - k0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= Nb || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > lim) s[kb][r] = -INFINITY;
         }
       }
     };
@@ -486,7 +491,7 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
         dsum = pair_sum(dsum);  // lanes l and l ^ 32 hold the two column halves of row qi
         if (g_e == 0) {
           LSE[lse_base + qi_e] = lse_row;
-          Dg[lse_base + qi_e] = dsum;
+          Dg[lse_base + qi_e] = -dsum;  // the backward's workspace holds -D_i
           L2[lse_base + qi_e] = lse_row * kLog2e;
         }
       } else {

@@ -213,13 +213,17 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
     float m_run = -INFINITY;  // reference maximum (log2 units) shared by numerator and normaliser
     float l_run = 0.f;        // the normaliser of this lane's query (P carries the factor 2^6)
 
+    // Slot (kb, r) holds key k0 + 4g + off(kb, r), off a compile-time constant below 64: a key is kept
+    // when it is at most the lane's last visible key (one compare and one select per score).
     auto apply_mask = [&](int k0, f32x16 (&s)[2]) {
+      const int last_key = CAUSAL ? min(qi, N - 1) : N - 1;
+      const int lim = last_key - k0 - 4 * g;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off > lim) s[kb][r] = -INFINITY;
         }
       }
     };
