@@ -258,7 +258,10 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[kb][r0 + e], c, bias));
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        // The low-half conversion leaves the high half of its register as it was, and the high-half
+        // conversion then writes it, so any value may fill it: p[0]'s own bits let the conversion
+        // write in place over p[0] (a zero there costs one move per word).
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
         pf[i] = word;
       }
