@@ -270,11 +270,12 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
     // 32 x 64 block (E4M3 1.0 = 0x38) with P^T; every element of the result holds the column sum,
     // so element 0 is taken. The conversion does not saturate: a probability above 464 becomes the
     // E4M3 NaN code, and the matrix unit carries it into its query's sum (both measured on gfx950).
-    auto colsum = [&](const i32x8& pf) {
-      const int one4 = 0x38383838;
-      const i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
-      return mfma_f8(ones, pf, f32x16{})[0];
-    };
+    // The all-ones operand is built once and made opaque to the compiler, which otherwise rebuilds
+    // the constant before every use (eight moves per tile and wave).
+    const int one4 = 0x38383838;
+    i32x8 ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+    asm volatile("" : "+v"(ones));
+    auto colsum = [&](const i32x8& pf) { return mfma_f8(ones, pf, f32x16{})[0]; };
 
     // O^T += V^T P^T: one 64-key MFMA per 32 output columns.
     auto pv = [&](const uint8_t* vbuf, const i32x8& pf) {
