@@ -91,7 +91,7 @@ hipError_t launch(const void* q, const void* k, const void* v, const void* o, co
   const bf16* O = static_cast<const bf16*>(o);
   const bf16* dO = static_cast<const bf16*>(dout);
   const long long rows = (long long)B * H * N;
-  float* D = static_cast<float*>(ws);  // workspace: D [B,H,N], then LSE * log2 e [B,H,N]
+  float* D = static_cast<float*>(ws);  // workspace: -D [B,H,N], then LSE * log2 e [B,H,N]
   float* L2 = D + rows;
   const int n_t = (N + 127) / 128;
   const int n_wg = CAUSAL ? (n_t + 1) / 2 : n_t;  // causal workgroups take a pair of tiles
@@ -128,7 +128,7 @@ hipError_t launch_varlen(const void* q, const void* k, const void* v, const void
   const bf16* V = static_cast<const bf16*>(v);
   const bf16* O = static_cast<const bf16*>(o);
   const bf16* dO = static_cast<const bf16*>(dout);
-  float* D = static_cast<float*>(ws);  // workspace: D [H,T], then LSE * log2 e [H,T]
+  float* D = static_cast<float*>(ws);  // workspace: -D [H,T], then LSE * log2 e [H,T]
   float* L2 = D + (size_t)H * T;
   const int n_t = (max_seqlen + 127) / 128;
   const int n_wg = CAUSAL ? (n_t + 1) / 2 : n_t;
@@ -158,7 +158,7 @@ hipError_t launch_varlen(const void* q, const void* k, const void* v, const void
 
 size_t bwd_varlen_workspace_bytes(int T, int H, int d) {
   (void)d;
-  return 2 * (size_t)H * T * sizeof(float);  // D and LSE * log2 e per (head, token) row
+  return 2 * (size_t)H * T * sizeof(float);  // -D and LSE * log2 e per (head, token) row
 }
 
 hipError_t launch_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -180,7 +180,7 @@ hipError_t launch_bwd_varlen(const void* q, const void* k, const void* v, const 
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
-  return 2 * (size_t)B * H * N * sizeof(float);  // D and LSE * log2 e per query row
+  return 2 * (size_t)B * H * N * sizeof(float);  // -D and LSE * log2 e per query row
 }
 
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
