@@ -181,13 +181,17 @@ __device__ __forceinline__ void fwd_bf16_job(const bf16* __restrict__ Q, const b
       const int lane_q = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
       const bf16x8* src = reinterpret_cast<const bf16x8*>(Q + q_base + (size_t)(q0 + (lane_q & 31)) * rs_q);
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        qf[kk] = src[2 * kk + (lane_q >> 5)];
-        if (neg) qf[kk] = -qf[kk];
-      }
+      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = src[2 * kk + (lane_q >> 5)];
     } else {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = bf16x8{};
+    }
+    // The sign flip: one XOR of the packed sign bits per dword, under a wave-uniform branch outside
+    // the divergent row test (an element-wise negation inside it cost four instructions per pair,
+    // issued whatever the sign).
+    if (neg) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[kk]) ^ 0x80008000u);
     }
 
     const int q_end = min(Nb, qt * FWD_BR + FWD_BR);

@@ -143,13 +143,15 @@ __global__ __launch_bounds__(F8_THREADS, 2) void fwd_fp8_kernel(
     if (qi < N) {
       const uint4* src = reinterpret_cast<const uint4*>(Q + q_base + (size_t)qi * HD);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        qf[kk] = cat16(src[4 * kk + 2 * g], src[4 * kk + 2 * g + 1]);
-        if (neg) qf[kk] ^= (int)0x80808080u;
-      }
+      for (int kk = 0; kk < KK; ++kk) qf[kk] = cat16(src[4 * kk + 2 * g], src[4 * kk + 2 * g + 1]);
     } else {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) qf[kk] = i32x8{};
+    }
+    // under a wave-uniform branch, outside the divergent row test
+    if (neg) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) qf[kk] ^= (int)0x80808080u;
     }
 
     const int q_end = min(N, qt * F8_BR + F8_BR);
