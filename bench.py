@@ -39,8 +39,11 @@ GRAPH_REPLAYS = 20  # timed replays of a graph of LEG_CALLS calls (launch-bound 
 
 # Ceilings measured by the ceiling microbenchmarks (csrc/ceilings.hip) on one MI355X, used only when
 # the executable is not available in this run: dense bf16 and E4M3 MFMA on the full chip after a
-# warm-up, and the HBM streaming read.
-COMMITTED_CEILINGS = {"mfma_bf16_tflops": 2435.4, "mfma_fp8_tflops": 4907.0, "hbm_read_gbs": 7146.0}
+# warm-up, on operands that barely switch (the same small values in every lane) and on operands
+# like the kernels' (random full-mantissa values, a new pair each instruction; under the chip's
+# power management the clock, and with it the rate, depends on the data), and the HBM streaming read.
+COMMITTED_CEILINGS = {"mfma_bf16_tflops": 2445.8, "mfma_fp8_tflops": 4921.3, "hbm_read_gbs": 7206.0,
+                      "mfma_bf16_random_tflops": 1820.4, "mfma_fp8_random_tflops": 3839.0}
 
 
 def parse(argv=None):
@@ -271,12 +274,15 @@ def rate_of(kind, amount, ms, ceil):
     """Algorithmic rate of `amount` FLOPs or bytes done in `ms`, with its fractions of the published
     peak and of the measured ceiling."""
     from roofline_attention_amd import ledger as L
-    if kind == "mfma":
+    if kind in ("mfma", "mfma8"):
         r = amount / (ms * 1e-3) / 1e12
-        return {"tflops": r, "frac_of_peak": r / L.PEAK_BF16_TFLOPS, "frac_of_ceiling": r / ceil["mfma_bf16_tflops"]}
-    if kind == "mfma8":
-        r = amount / (ms * 1e-3) / 1e12
-        return {"tflops": r, "frac_of_peak": r / L.PEAK_FP8_TFLOPS, "frac_of_ceiling": r / ceil["mfma_fp8_tflops"]}
+        fp8 = kind == "mfma8"
+        out = {"tflops": r, "frac_of_peak": r / (L.PEAK_FP8_TFLOPS if fp8 else L.PEAK_BF16_TFLOPS),
+               "frac_of_ceiling": r / ceil["mfma_fp8_tflops" if fp8 else "mfma_bf16_tflops"]}
+        data = ceil.get("mfma_fp8_random_tflops" if fp8 else "mfma_bf16_random_tflops")
+        if data:  # the same instruction's rate on operands like the kernel's
+            out["frac_of_data_ceiling"] = r / data
+        return out
     r = amount / (ms * 1e-3) / 1e9
     return {"gbs": r, "frac_of_peak": r / L.PEAK_HBM_GBS, "frac_of_ceiling": r / ceil["hbm_read_gbs"]}
 
@@ -358,6 +364,7 @@ def main():
     roof = {"kernel": dom, "bound": "mfma", "achieved": d["tflops"], "peak": L.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": d["frac_of_peak"], "traffic": measured_traffic(dom),
             "ceiling": ceil["mfma_bf16_tflops"], "frac_of_ceiling": d["frac_of_ceiling"],
+            "data_ceiling": ceil.get("mfma_bf16_random_tflops"), "frac_of_data_ceiling": d.get("frac_of_data_ceiling"),
             "avg_ms": d["mean_ms"], "median_ms": d["median_ms"], "p10_ms": d["p10_ms"], "p90_ms": d["p90_ms"],
             "min_ms": d["min_ms"], "algorithmic_per_launch": amount,
             "samples_ms": [round(x, 5) for x in per_kernel[dom]]}

@@ -6,7 +6,7 @@
 //   mfma_bf16 / mfma_fp8: full-chip rate of independent v_mfma_f32_32x32x16_bf16 and
 //                         v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3), in TFLOP/s (timed with events),
 //                         and the cycles one instruction occupies the matrix pipe (clock64, one
-//                         wave per SIMD);
+//                         wave per SIMD); the *_random variants feed operands like real data;
 //   hbm_read, hbm_copy:   streaming read (sum of a 2 GiB buffer, non-temporal 16-byte loads,
 //                         8 workgroups per CU, grid-stride) and copy, in GB/s;
 //   lds_read:             bytes per clock per CU for ds_read_b128 and ds_read_b64_tr_b16;
@@ -53,23 +53,59 @@ void warm_up(F launch) {
 
 constexpr int MFMA_IT = 4000;
 
-template <int KIND>  // 0: bf16 32x32x16, 1: E4M3 32x32x64
+// KIND 0: bf16 32x32x16, 1: E4M3 32x32x64, both on operands that are the same small values in every
+// lane and every instruction; 2 and 3: the same instructions on operands like the attention kernels'
+// (per lane pseudo-random values with full mantissas, a different operand pair for each of eight
+// consecutive instructions), which switch far more of the matrix datapath: under the chip's power
+// management the clock, and with it the rate, depends on the data.
+template <int KIND>
 __global__ __launch_bounds__(256) void mfma_kernel(float* out, unsigned long long* cyc, int seed) {
+  constexpr bool RANDOM = KIND >= 2;
+  constexpr bool FP8 = KIND == 1 || KIND == 3;
+  constexpr int SETS = RANDOM ? 8 : 1;
   f32x16 acc[4] = {};
-  bf16x8 a, b;
-  i32x8 wa, wb;
-  for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(float)((seed + i) & 3);
-    b[i] = (__bf16)(float)((i - seed) & 3);
-    wa[i] = 0x38383838 + i;
-    wb[i] = 0x38383838 - i;
+  bf16x8 a[SETS], b[SETS];
+  i32x8 wa[SETS], wb[SETS];
+  uint32_t x = (uint32_t)seed * 2654435761u ^ (uint32_t)(blockIdx.x * 256 + threadIdx.x + 1) * 0x9E3779B9u;
+  auto next = [&]() {  // xorshift32
+    x ^= x << 13;
+    x ^= x >> 17;
+    x ^= x << 5;
+    return x;
+  };
+  for (int j = 0; j < SETS; ++j) {
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (RANDOM) {
+        // uniform in [-2, 2) with a full 8-bit mantissa; E4M3 codes with random sign, exponent
+        // 4..11 and mantissa (finite, no NaN code)
+        a[j][i] = (__bf16)((float)((int)(next() & 0xffff) - 32768) * (1.f / 16384.f));
+        b[j][i] = (__bf16)((float)((int)(next() & 0xffff) - 32768) * (1.f / 16384.f));
+        uint32_t ca = 0, cb = 0;
+        for (int byte = 0; byte < 4; ++byte) {
+          const uint32_t r1 = next(), r2 = next();
+          ca |= ((r1 & 0x80) | (((r1 >> 8) & 7) + 4) << 3 | ((r1 >> 16) & 7)) << (8 * byte);
+          cb |= ((r2 & 0x80) | (((r2 >> 8) & 7) + 4) << 3 | ((r2 >> 16) & 7)) << (8 * byte);
+        }
+        wa[j][i] = (int)ca;
+        wb[j][i] = (int)cb;
+      } else {
+        a[j][i] = (__bf16)(float)((seed + i) & 3);
+        b[j][i] = (__bf16)(float)((i - seed) & 3);
+        wa[j][i] = 0x38383838 + i;
+        wb[j][i] = 0x38383838 - i;
+      }
+    }
   }
   const unsigned long long t0 = clock64();
-  for (int it = 0; it < MFMA_IT; ++it) {
+  for (int it = 0; it < MFMA_IT / SETS * SETS; it += SETS) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (KIND == 0) acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[q], 0, 0, 0);
-      else acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, wb, acc[q], 0, 0, 0, 127, 0, 127);
+    for (int j = 0; j < SETS; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int o = (j + q) % SETS;  // a different operand pair for each of the four chains
+        if constexpr (!FP8) acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[o], b[o], acc[q], 0, 0, 0);
+        else acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[o], wb[o], acc[q], 0, 0, 0, 127, 0, 127);
+      }
     }
   }
   const unsigned long long t1 = clock64();
@@ -100,7 +136,7 @@ void mfma_rate(int cus, double& tflops, double& cycles_per_inst) {
   CHECK(hipEventElapsedTime(&ms, e0, e1));
   unsigned long long c0 = 0;
   CHECK(hipMemcpy(&c0, cyc, 8, hipMemcpyDeviceToHost));
-  const double flops_per_inst = KIND == 0 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
+  const double flops_per_inst = (KIND == 0 || KIND == 2) ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
   const double insts = (double)kTimed * grid * 4 /* waves */ * MFMA_IT * 4;
   tflops = insts * flops_per_inst / (ms * 1e-3) / 1e12;
   // one wave per SIMD issuing independent MFMAs: cycles between its instructions = pipe occupancy
@@ -329,9 +365,11 @@ int main() {
   int dev = 0, cus = 0;
   CHECK(hipGetDevice(&dev));
   CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-  double bf16_tf, bf16_cyc, fp8_tf, fp8_cyc, rd, cp;
+  double bf16_tf, bf16_cyc, fp8_tf, fp8_cyc, bf16r_tf, bf16r_cyc, fp8r_tf, fp8r_cyc, rd, cp;
   mfma_rate<0>(cus, bf16_tf, bf16_cyc);
   mfma_rate<1>(cus, fp8_tf, fp8_cyc);
+  mfma_rate<2>(cus, bf16r_tf, bf16r_cyc);
+  mfma_rate<3>(cus, fp8r_tf, fp8r_cyc);
   hbm(cus, rd, cp);
   const double lds128 = lds_bytes_per_clk<0>(cus), ldstr = lds_bytes_per_clk<1>(cus);
   const double fma_c = valu_cycles<0>(), exp_c = valu_cycles<1>();
@@ -342,7 +380,10 @@ int main() {
          "\"hbm_copy_gbs\": %.0f, \"lds_b128_bytes_per_clk_cu\": %.1f, \"lds_tr_b16_bytes_per_clk_cu\": %.1f, "
          "\"valu_fma_cycles\": %.2f, \"valu_exp_cycles\": %.2f, \"coexec_cycles_mfma_only\": %.1f, "
          "\"coexec_cycles_valu_only\": %.1f, \"coexec_cycles_split_waves\": %.1f, "
-         "\"coexec_cycles_interleaved\": %.1f}\n",
-         cus, bf16_tf, bf16_cyc, fp8_tf, fp8_cyc, rd, cp, lds128, ldstr, fma_c, exp_c, co0, co1, co2, co3);
+         "\"coexec_cycles_interleaved\": %.1f, \"mfma_bf16_random_tflops\": %.1f, "
+         "\"mfma_bf16_random_cycles_per_inst\": %.2f, \"mfma_fp8_random_tflops\": %.1f, "
+         "\"mfma_fp8_random_cycles_per_inst\": %.2f}\n",
+         cus, bf16_tf, bf16_cyc, fp8_tf, fp8_cyc, rd, cp, lds128, ldstr, fma_c, exp_c, co0, co1, co2, co3, bf16r_tf,
+         bf16r_cyc, fp8r_tf, fp8r_cyc);
   return 0;
 }

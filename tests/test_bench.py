@@ -63,6 +63,9 @@ def test_rates_against_peak_and_ceiling():
     ceil = {"mfma_bf16_tflops": 2000.0, "mfma_fp8_tflops": 4000.0, "hbm_read_gbs": 7000.0}
     r = bench.rate_of("mfma", 2.5e12, 1.0, ceil)  # 2.5 TFLOP in 1 ms
     assert abs(r["tflops"] - 2500.0) < 1e-9 and abs(r["frac_of_ceiling"] - 1.25) < 1e-12
+    assert "frac_of_data_ceiling" not in r  # no data-dependent ceiling given
+    r = bench.rate_of("mfma", 2.5e12, 1.0, dict(ceil, mfma_bf16_random_tflops=1250.0))
+    assert abs(r["frac_of_data_ceiling"] - 2.0) < 1e-12
     r = bench.rate_of("hbm", 7e9, 1.0, ceil)  # 7 GB in 1 ms
     assert abs(r["gbs"] - 7000.0) < 1e-9 and abs(r["frac_of_peak"] - 0.875) < 1e-12
 
