@@ -622,11 +622,13 @@ __device__ __forceinline__ void bwd_dq_job(
     const int t_mask = CAUSAL ? max(0, n_kt - 2) : n_kt;
     stage(0, 0);
     int t = 0;
-    // At d = 128, two tiles per trip: each tile's LDS stage is then a constant that folds into the
-    // LDS reads' immediate offsets, where a stage chosen at run time cost 42 address instructions per
-    // tile (the kernel has no registers left to hold the per-lane offsets of both stages). At d = 64
-    // the unrolled loop needs registers beyond three waves per SIMD, so it keeps one tile per trip.
-    if constexpr (HD == 128) {
+    // At d = 128 without the mask, two tiles per trip: each tile's LDS stage is then a constant that
+    // folds into the LDS reads' immediate offsets, where a stage chosen at run time cost 42 address
+    // instructions per tile (the kernel has no registers left to hold the per-lane offsets of both
+    // stages). The causal kernel keeps one tile per trip: with the masked tiles' loop beside it the
+    // unrolled loop spilled 48 bytes per lane, and the spill-free loop runs as fast. At d = 64 the
+    // unrolled loop needs registers beyond three waves per SIMD.
+    if constexpr (HD == 128 && !CAUSAL) {
       for (; t + 1 < t_mask; t += 2) {  // t starts at 0: stage 0 first
         tile(0, t, NoMask{});
         tile(1, t + 1, NoMask{});
